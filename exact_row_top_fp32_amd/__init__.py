@@ -1,0 +1,155 @@
+"""Exact per-row top-k over long, ragged fp32 rows on MI355X (gfx950).
+
+A thin ctypes binding of ``libexact_topk.so`` (C ABI in ``include/exact_topk.h``).
+The functions keep the C names and only marshal torch tensors into pointers,
+sizes and the current HIP stream; every step of the selection runs in the HIP
+kernels. There is no fallback: if the library is not built, or the tensors do
+not live on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity",
+    "TopKError", "library_path", "PATH_AUTO", "PATH_LDS", "PATH_SAMPLED", "PATH_FULLROW",
+    "ROW_EMPTY", "ROW_ALL", "ROW_LDS", "ROW_SAMPLED", "ROW_FULL_OVERFLOW",
+    "ROW_FULL_UNDERFLOW", "ROW_FULL_FORCED", "MAX_K",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libexact_topk.so")
+
+MAX_K = 2048
+PATH_AUTO, PATH_LDS, PATH_SAMPLED, PATH_FULLROW = 0, 1, 2, 3
+(ROW_EMPTY, ROW_ALL, ROW_LDS, ROW_SAMPLED, ROW_FULL_OVERFLOW, ROW_FULL_UNDERFLOW,
+ ROW_FULL_FORCED) = range(7)
+
+
+class TopKError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("force_path", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("row_stats", ctypes.c_void_p)]
+
+
+_lib = None
+_ARGS = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+         ctypes.c_void_p]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(
+                f"{library_path} is missing: build it with `python -m exact_row_top_fp32_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        lib.topk_select.restype = ctypes.c_int
+        lib.topk_select.argtypes = _ARGS
+        lib.topk_select_ex.restype = ctypes.c_int
+        lib.topk_select_ex.argtypes = _ARGS + [ctypes.POINTER(_Options)]
+        lib.topk_status_string.restype = ctypes.c_char_p
+        lib.topk_status_string.argtypes = [ctypes.c_int]
+        lib.topk_max_capacity.restype = ctypes.c_int32
+        lib.topk_max_capacity.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def topk_status_string(status: int) -> str:
+    return _load().topk_status_string(status).decode()
+
+
+def topk_max_capacity() -> int:
+    return int(_load().topk_max_capacity())
+
+
+def _device_ptr(t: torch.Tensor | None, name: str, dtype: torch.dtype):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream):
+    if scores.dim() != 2 or (scores.size(1) > 1 and scores.stride(1) != 1):
+        raise ValueError("scores must be 2-D with unit column stride")
+    batch = scores.size(0)
+    row_stride = scores.stride(0) if batch > 1 else max(scores.size(1), 1)
+    if n_cols is None:
+        n_cols = scores.size(1)
+    if n_cols > scores.size(1):
+        raise ValueError("n_cols exceeds the width of scores")
+    if lengths is not None:
+        if lengths.dim() != 1 or lengths.size(0) != batch or not lengths.is_contiguous():
+            raise ValueError("lengths must be a contiguous [batch] tensor")
+    if out is None:
+        out = torch.empty((batch, k), dtype=torch.int32, device=scores.device)
+    elif out.shape != (batch, k) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [batch, k] tensor")
+    pt_stride = 0
+    if page_table is not None:
+        if page_table.dim() != 2 or page_table.size(0) != batch or (
+                page_table.size(1) > 1 and page_table.stride(1) != 1):
+            raise ValueError("page_table must be [batch, pages] with unit column stride")
+        pt_stride = page_table.stride(0) if batch > 1 else page_table.size(1)
+    if stream is None:
+        stream = torch.cuda.current_stream(scores.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    args = (
+        _device_ptr(scores, "scores", torch.float32), batch, row_stride, n_cols,
+        _device_ptr(lengths, "lengths", torch.int32), int(k),
+        _device_ptr(out, "out", torch.int32), _device_ptr(page_table, "page_table", torch.int32),
+        pt_stride, int(page_size), handle,
+    )
+    return args, out
+
+
+def _check(status: int):
+    if status != 0:
+        raise TopKError(status, topk_status_string(status))
+
+
+def topk_select(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
+                out: torch.Tensor | None = None, page_table: torch.Tensor | None = None,
+                page_size: int = 0, *, n_cols: int | None = None, stream=None) -> torch.Tensor:
+    """Exact top-k of every row of ``scores`` (fp32 ``[batch, >= n_cols]``).
+
+    Returns ``out`` (int32 ``[batch, k]``): positions (or page-table slots) of
+    each row's k best scores in no particular order, ``-1`` past
+    ``min(k, lengths[b])``. Asynchronous on ``stream`` (default: the current
+    torch stream).
+    """
+    args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream)
+    _check(_load().topk_select(*args))
+    return out
+
+
+def topk_select_ex(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
+                   out: torch.Tensor | None = None, page_table: torch.Tensor | None = None,
+                   page_size: int = 0, *, n_cols: int | None = None, stream=None,
+                   force_path: int = PATH_AUTO, capacity: int = 0,
+                   row_stats: torch.Tensor | None = None) -> torch.Tensor:
+    """``topk_select`` with path forcing, a capacity override and row statistics.
+
+    ``row_stats`` (int32 ``[batch, 2]``, contiguous) receives the path code
+    and the sampled survivor count (or the length) of every row.
+    """
+    args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream)
+    if row_stats is not None and (row_stats.shape != (scores.size(0), 2) or not row_stats.is_contiguous()):
+        raise ValueError("row_stats must be a contiguous [batch, 2] tensor")
+    opt = _Options(int(force_path), int(capacity), _device_ptr(row_stats, "row_stats", torch.int32))
+    _check(_load().topk_select_ex(*args, ctypes.byref(opt)))
+    return out

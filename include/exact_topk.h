@@ -1,0 +1,133 @@
+/*
+ * exact_topk.h -- C ABI of the gfx950 library for exact per-row top-k over
+ * long, ragged fp32 score rows (the decode-time selection of a sparse-
+ * attention indexer).
+ *
+ * The operation (sources by page and section):
+ *  - "dsv4.1: Top-k kernels and candidate selection" (sglang PR #39648
+ *    report), code excerpts, docstring of the bf16 top-k entry: row b selects
+ *    the k best of its first lengths[b] scores, in no particular order; -1
+ *    fills every slot past min(k, lengths[b]); in paged mode a selected index
+ *    i is written as page_table[b, i / page_size] * page_size + i % page_size;
+ *    k is at most 2048.
+ *  - same page, motivation: -inf is a legal score and is selected like any
+ *    other; lengths are non-negative, 0 meaning an idle row.
+ *  - "Fix incorrect sparse-attention top-k selection when candidate bins
+ *    overflow" (sglang PR #37625), modifications and comment thread: the
+ *    selected-value multiset is exact even when one coarse bin holds more
+ *    candidates than any buffer; only equal scores may trade places.
+ *  - vLLM PR #56346 report, implementation items 1-3: one launch serves long
+ *    and short rows, lengths stay on the device, grid = one workgroup per row.
+ *
+ * Result, exactly: with L = clamp(lengths[b], 0, n_cols) and m = min(k, L),
+ * slots [0, m) of out row b hold the m positions of [0, L) that rank first
+ * by value (descending; +0 above -0; among equal values the lower index
+ * first), in an unspecified order, and slots [m, k) hold -1. Because equal
+ * values go to the lower index, the selected set is unique: every call, and
+ * every internal path, returns the same set.
+ *
+ * Memory: every pointer argument is a DEVICE pointer owned by the caller.
+ * The library allocates, frees and retains nothing; it reads scores[b, 0:L),
+ * lengths[0:batch) and the page-table entries of pages that hold a selected
+ * position, and writes only out_idx[0:batch, 0:k).
+ *
+ * Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the default
+ * stream) and never synchronise. Argument errors are returned synchronously
+ * as a status code before anything is launched; device data (lengths, page
+ * table contents) is never an error: lengths are clamped to [0, n_cols].
+ * NaN inside [0, L) is outside the contract: the call stays memory-safe, but
+ * which positions it selects is unspecified. The library keeps no global
+ * state and is safe to call from several host threads.
+ */
+#ifndef EXACT_TOPK_H
+#define EXACT_TOPK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TOPK_OK 0
+#define TOPK_ERR_ARG 1    /* negative or oversized size, row_stride < n_cols, NULL data pointer,
+                             page_size < 1 or page_table_stride too small, bad option value */
+#define TOPK_ERR_K 2      /* k outside [1, TOPK_MAX_K] */
+#define TOPK_ERR_ALIGN 3  /* scores not 16-byte aligned, or row_stride % 4 != 0 with batch > 1 */
+#define TOPK_ERR_LAUNCH 5 /* the HIP launch itself failed (e.g. no gfx950 device) */
+
+#define TOPK_MAX_K 2048
+
+/* internal paths (for topk_options.force_path and row statistics) */
+#define TOPK_PATH_AUTO 0
+#define TOPK_PATH_LDS 1      /* whole row held in LDS, exact select there (rows <= capacity) */
+#define TOPK_PATH_SAMPLED 2  /* sampled cutoff, one streaming pass, exact select on survivors */
+#define TOPK_PATH_FULLROW 3  /* full-row exact: histogram-only passes, one emission pass */
+
+/* row statistics codes, written to row_stats[2*b] */
+#define TOPK_ROW_EMPTY 0          /* m == 0: every slot -1 */
+#define TOPK_ROW_ALL 1            /* L <= k: every position selected */
+#define TOPK_ROW_LDS 2
+#define TOPK_ROW_SAMPLED 3
+#define TOPK_ROW_FULL_OVERFLOW 4  /* sampled survivors exceeded the capacity */
+#define TOPK_ROW_FULL_UNDERFLOW 5 /* fewer sampled survivors than m */
+#define TOPK_ROW_FULL_FORCED 6    /* full-row path chosen by the caller, or LDS forced on a row above capacity */
+
+/*
+ * topk_select -- exact top-k of every row.
+ *
+ *  scores             fp32 [batch, row_stride], row-major; 16-byte aligned base and
+ *                     row_stride % 4 == 0 (when batch > 1)
+ *  batch              rows, 0 <= batch <= INT32_MAX (0: no-op, TOPK_OK)
+ *  row_stride         elements between row starts, >= n_cols
+ *  n_cols             largest valid length, 0 <= n_cols <= INT32_MAX
+ *  lengths            int32 [batch] valid scores per row, or NULL (all rows n_cols);
+ *                     values are clamped to [0, n_cols]
+ *  k                  slots per row, 1 <= k <= TOPK_MAX_K
+ *  out_idx            int32 [batch, k], contiguous
+ *  page_table         int32 [batch, page_table_stride] or NULL for raw positions
+ *  page_table_stride  elements between page-table rows, >= ceil(n_cols / page_size)
+ *  page_size          positions per page, >= 1 when page_table is given
+ *  hip_stream         hipStream_t to launch on
+ * Returns TOPK_OK or an error code; on error nothing was launched.
+ * The caller keeps slot values inside int32 (page * page_size + offset).
+ */
+int topk_select(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                const int32_t* lengths, int32_t k, int32_t* out_idx,
+                const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                void* hip_stream);
+
+/*
+ * Diagnostic and test controls for topk_select_ex. A zeroed struct (or a NULL
+ * pointer) gives exactly topk_select. The selected set never depends on them:
+ * every path returns the same unique set.
+ *  force_path  TOPK_PATH_* for every row with k < L (rows with L <= k take the
+ *              direct path); LDS forced on a row longer than the capacity runs
+ *              the full-row path instead
+ *  capacity    survivor capacity in entries, 1..topk_max_capacity() (0 = maximum);
+ *              a small value makes the overflow fallback easy to reach
+ *  row_stats   device int32 [batch, 2] or NULL: [2b] = TOPK_ROW_* code,
+ *              [2b+1] = survivor count of the sampled pass (or L on other paths)
+ */
+typedef struct topk_options {
+    int32_t force_path;
+    int32_t capacity;
+    int32_t* row_stats;
+} topk_options;
+
+int topk_select_ex(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                   const int32_t* lengths, int32_t k, int32_t* out_idx,
+                   const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                   void* hip_stream, const topk_options* options);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* topk_status_string(int status);
+
+/* Largest survivor capacity (entries held in LDS per workgroup). */
+int32_t topk_max_capacity(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_TOPK_H */

@@ -1,0 +1,107 @@
+"""The C ABI without a GPU: exported symbols and host-side argument checks.
+
+Every function declared in include/*.h must be exported by the built library.
+Argument errors are decided on the host before any HIP call, so they are
+checked here with pointers that are never dereferenced.
+"""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "exact_row_top_fp32_amd", "libexact_topk.so")
+
+ARGS = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+        ctypes.c_void_p]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("force_path", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("row_stats", ctypes.c_void_p)]
+
+
+def header_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(topk_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from exact_row_top_fp32_amd import build
+        build.build()
+    lib = ctypes.CDLL(LIB)
+    lib.topk_select.argtypes = ARGS
+    lib.topk_select.restype = ctypes.c_int
+    lib.topk_select_ex.argtypes = ARGS + [ctypes.POINTER(Options)]
+    lib.topk_select_ex.restype = ctypes.c_int
+    lib.topk_status_string.restype = ctypes.c_char_p
+    lib.topk_max_capacity.restype = ctypes.c_int32
+    return lib
+
+
+def test_header_declares_the_entry_points():
+    assert header_functions() == sorted(
+        ["topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    dyn = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    for name in header_functions():
+        assert re.search(rf"\bT {name}\b", dyn), name
+
+
+def test_library_targets_gfx950():
+    out = subprocess.run(["strings", LIB], capture_output=True, text=True).stdout
+    assert "gfx950" in out
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def call(lib, scores=FAKE, batch=4, row_stride=1024, n_cols=1024, lengths=None, k=16,
+         out=FAKE, page_table=None, pt_stride=0, page_size=0, opt=None):
+    a = (scores, batch, row_stride, n_cols, lengths, k, out, page_table, pt_stride, page_size, None)
+    if opt is None:
+        return lib.topk_select(*a)
+    return lib.topk_select_ex(*a, ctypes.byref(opt))
+
+
+def test_host_argument_checks(lib):
+    assert call(lib, k=0) == 2 and call(lib, k=2049) == 2 and call(lib, k=-5) == 2
+    assert call(lib, batch=-1) == 1
+    assert call(lib, batch=2**31) == 1
+    assert call(lib, row_stride=1000, n_cols=1024) == 1
+    assert call(lib, n_cols=-1) == 1
+    assert call(lib, scores=None) == 1 and call(lib, out=None) == 1
+    assert call(lib, scores=FAKE + 4) == 3
+    assert call(lib, row_stride=1026, n_cols=1024) == 3
+    assert call(lib, page_table=FAKE, page_size=0, pt_stride=64) == 1
+    assert call(lib, page_table=FAKE, page_size=64, pt_stride=15) == 1
+    assert call(lib, opt=Options(7, 0, None)) == 1
+    assert call(lib, opt=Options(0, lib.topk_max_capacity() + 1, None)) == 1
+    assert call(lib, opt=Options(0, -1, None)) == 1
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert call(lib, batch=0, scores=None, out=None) == 0
+    assert call(lib, batch=0, scores=None, out=None, opt=Options(3, 5, None)) == 0
+
+
+def test_status_strings(lib):
+    for code in (0, 1, 2, 3, 5, 99):
+        assert lib.topk_status_string(code)
+    assert lib.topk_max_capacity() >= 4096

@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case compares the GPU's output with the oracle's on the same seeded
+inputs: -1 slots, index range and uniqueness, the selected-value multiset bit
+for bit, and the selected index set itself (both sides take the lowest indices
+among ties at the cutoff, so the set is unique). Outputs sit between guard
+regions that must come back untouched, and positions past each row's length
+hold NaN, which would rank first if any kernel read it.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from topk_check import check, check_fast_raw
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+CANARY = 0x5A5A5A5A - 2**32  # as int32
+
+
+@pytest.fixture(scope="session")
+def topk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_row_top_fp32_amd as topk_mod
+    topk_mod._load()
+    return topk_mod
+
+
+_dev_cache = {}
+
+
+def to_dev(a):
+    key = id(a)
+    if key not in _dev_cache:
+        _dev_cache[key] = (a, torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    return _dev_cache[key][1]
+
+
+def say(*msg):
+    print(*msg, flush=True)
+
+
+def run(topk, wl, *, k=None, force=0, capacity=0, lengths=None, scores_dev=None,
+        n_cols=None, want_stats=False):
+    """Launch through the C ABI with guarded output; returns (out, stats)."""
+    k = wl.k if k is None else k
+    B = wl.batch
+    s = to_dev(wl.scores) if scores_dev is None else scores_dev
+    ln = to_dev(wl.lengths if lengths is None else lengths)
+    pt = to_dev(wl.page_table) if wl.page_table is not None else None
+    buf = torch.full((B * k + 2 * GUARD,), CANARY, dtype=torch.int32, device="cuda")
+    out = buf[GUARD:GUARD + B * k].view(B, k)
+    stats = torch.full((B, 2), -7, dtype=torch.int32, device="cuda") if want_stats else None
+    say(f"  gpu call: {wl.name} k={k} force={force} cap={capacity}")
+    topk.topk_select_ex(s, ln, k, out, pt, wl.page_size, n_cols=n_cols or wl.n_cols,
+                        force_path=force, capacity=capacity, row_stats=stats)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert np.all(h[:GUARD] == CANARY) and np.all(h[GUARD + B * k:] == CANARY), "write outside out"
+    return h[GUARD:GUARD + B * k].reshape(B, k), (stats.cpu().numpy() if want_stats else None)
+
+
+def expect(wl, k=None, lengths=None, n_cols=None):
+    return oracle.topk(wl.scores, wl.lengths if lengths is None else lengths,
+                       wl.k if k is None else k, n_cols=n_cols or wl.n_cols,
+                       page_table=wl.page_table, page_size=wl.page_size)
+
+
+def assert_parity(wl, got, want, k=None, lengths=None, n_cols=None):
+    fails = check(wl.scores, wl.lengths if lengths is None else lengths, n_cols or wl.n_cols,
+                  wl.k if k is None else k, got, want, page_table=wl.page_table,
+                  page_size=wl.page_size)
+    assert not fails, "\n".join(fails)
+
+
+PATHS = [0, 1, 2, 3]
+PATH_IDS = ["auto", "lds", "sampled", "fullrow"]
+
+
+# ----------------------------------------------------------------------------
+# the five workloads
+# ----------------------------------------------------------------------------
+
+@pytest.fixture(scope="session")
+def c1():
+    return synth.c1()
+
+
+@pytest.mark.parametrize("force", PATHS, ids=PATH_IDS)
+def test_c1_every_path(topk, c1, force):
+    got, stats = run(topk, c1, force=force, want_stats=True)
+    assert_parity(c1, got, expect(c1))
+
+
+@pytest.fixture(scope="session", params=[512, 1024, 2048])
+def c2(request):
+    return synth.c2(request.param)
+
+
+@pytest.mark.parametrize("force", PATHS, ids=PATH_IDS)
+def test_c2_adversarial_every_path(topk, c2, force):
+    got, stats = run(topk, c2, force=force, want_stats=True)
+    want = expect(c2)
+    assert_parity(c2, got, want)
+    if force == 0:
+        say("  row paths:", dict(zip(*np.unique(stats[:, 0], return_counts=True))))
+
+
+def test_c2_small_capacity_forces_overflow(topk, c2):
+    got, stats = run(topk, c2, force=2, capacity=300, want_stats=True)
+    assert_parity(c2, got, expect(c2))
+    assert np.all(stats[:, 0] >= 4), "every row must fall back when m exceeds the capacity"
+
+
+@pytest.fixture(scope="session")
+def c3():
+    return synth.c3()
+
+
+@pytest.fixture(scope="session")
+def c4():
+    return synth.c4()
+
+
+def test_c3_decode_batch_all_rows(topk, c3):
+    got, stats = run(topk, c3, want_stats=True)
+    want = expect(c3)
+    bad = check_fast_raw(got, want, c3.lengths, c3.n_cols, c3.k)
+    assert not bad, f"rows differing from the oracle: {bad[:10]}"
+    assert_parity(c3, got, want)
+    paths = dict(zip(*np.unique(stats[:, 0], return_counts=True)))
+    say("  c3 row paths:", paths, "survivors min/mean/max:",
+        stats[:, 1].min(), stats[:, 1].mean(), stats[:, 1].max())
+
+
+def test_c4_decode_batch_all_rows(topk, c4):
+    got, stats = run(topk, c4, want_stats=True)
+    want = expect(c4)
+    bad = check_fast_raw(got, want, c4.lengths, c4.n_cols, c4.k)
+    assert not bad, f"rows differing from the oracle: {bad[:10]}"
+    paths = dict(zip(*np.unique(stats[:, 0], return_counts=True)))
+    say("  c4 row paths:", paths, "survivors min/mean/max:",
+        stats[:, 1].min(), stats[:, 1].mean(), stats[:, 1].max())
+
+
+@pytest.mark.parametrize("force", [1, 3], ids=["lds-forced", "fullrow"])
+def test_c3_rows_forced_paths(topk, c3, force):
+    # 64 rows of the decode batch through the fallback paths
+    sub = synth.Workload("c3_first64", 3, c3.scores[:64], c3.lengths[:64], c3.n_cols, c3.k)
+    got, _ = run(topk, sub, force=force)
+    assert not check_fast_raw(got, expect(sub), sub.lengths, sub.n_cols, sub.k)
+
+
+@pytest.mark.parametrize("global_pool", [False, True], ids=["row_perm", "global_pool"])
+@pytest.mark.parametrize("force", PATHS, ids=PATH_IDS)
+def test_c5_paged(topk, force, global_pool):
+    wl = synth.c5(global_pool=global_pool)
+    got, _ = run(topk, wl, force=force)
+    assert_parity(wl, got, expect(wl))
+
+
+# ----------------------------------------------------------------------------
+# boundaries and edge cases
+# ----------------------------------------------------------------------------
+
+def test_length_boundaries(topk):
+    k, W = 512, 20000
+    cap = topk.topk_max_capacity()
+    lens = [-1, -100, 0, 1, k - 1, k, k + 1, cap - 1, cap, cap + 1, 2 * cap, W - 1, W, W + 17]
+    wl = synth.mixed_rows(["normal"] * len(lens), W, k, seed=21)
+    wl.lengths = np.array(lens, np.int32)
+    synth.poison_tails(wl.scores, np.clip(wl.lengths, 0, W))
+    for force in PATHS:
+        got, stats = run(topk, wl, force=force, want_stats=True)
+        assert_parity(wl, got, expect(wl))
+
+
+@pytest.mark.parametrize("k", [1, 2, 63, 64, 65, 2047, 2048])
+def test_k_range(topk, k):
+    wl = synth.mixed_rows(["normal", "heavy_ties", "constant", "signed_zero", "ascending"], 9000, k, seed=22)
+    wl.lengths = np.array([9000, 9000, 2048, 2049, 5000], np.int32)
+    synth.poison_tails(wl.scores, wl.lengths)
+    for force in PATHS:
+        got, _ = run(topk, wl, k=k, force=force)
+        assert_parity(wl, got, expect(wl, k=k), k=k)
+
+
+def test_offset_view_and_stride(topk):
+    rng = np.random.default_rng(23)
+    base = rng.standard_normal((10, 12000)).astype(np.float32)
+    dev = torch.from_numpy(base).cuda()
+    view = dev[2:8, 16:11016]   # base offset of 16 floats, row stride 12000 > n_cols 11000
+    host = base[2:8, 16:11016]
+    lengths = np.array([11000, 10000, 500, 0, 9001, 11000], np.int32)
+    wl = synth.Workload("offset_view", 23, host, lengths, 11000, 700)
+    for force in PATHS:
+        got, _ = run(topk, wl, force=force, scores_dev=view)
+        assert_parity(wl, got, expect(wl))
+
+
+def test_lengths_null_means_full_rows(topk):
+    wl = synth.mixed_rows(["normal", "lowbits10", "onebin"], 10000, 300, seed=24)
+    s = to_dev(wl.scores)
+    out = topk.topk_select(s, None, 300)
+    torch.cuda.synchronize()
+    assert_parity(wl, out.cpu().numpy(), expect(wl))
+
+
+def test_exact_capacity_boundary(topk):
+    # survivors exactly at the capacity are kept; one fewer slot forces the fallback
+    wl = synth.mixed_rows(["normal"] * 8 + ["crowd4096"] * 8, 60000, 1024, seed=25)
+    _, stats = run(topk, wl, force=2, want_stats=True)
+    want = expect(wl)
+    for b in range(wl.batch):
+        if stats[b, 0] != 3:
+            continue
+        n = int(stats[b, 1])
+        row = synth.Workload("row", 25, wl.scores[b:b + 1], wl.lengths[b:b + 1], wl.n_cols, wl.k)
+        for cap, ok_code in ((n, 3), (n - 1, 4)):
+            if not 1 <= cap <= topk.topk_max_capacity():
+                continue
+            got, st = run(topk, row, force=2, capacity=cap, want_stats=True)
+            assert st[0, 0] == ok_code, (b, n, cap, st[0])
+            assert_parity(row, got, want[b:b + 1])
+
+
+def test_lds_capacity_boundary(topk):
+    cap = 3000
+    wl = synth.mixed_rows(["normal", "heavy_ties", "normal", "heavy_ties"], 4000, 256, seed=26)
+    wl.lengths = np.array([cap, cap, cap + 1, cap + 1], np.int32)
+    synth.poison_tails(wl.scores, wl.lengths)
+    got, stats = run(topk, wl, capacity=cap, want_stats=True)
+    assert list(stats[:, 0]) == [2, 2, stats[2, 0], stats[3, 0]] and stats[2, 0] >= 3
+    assert_parity(wl, got, expect(wl))
+
+
+def test_repeated_calls_same_set_and_changed_inputs(topk):
+    # the same device buffers reused with new lengths and flipped scores
+    k = 512
+    wl = synth.mixed_rows(["normal", "clustered_peaks", "onebin", "neginf_half"] * 2, 40000, k, seed=27)
+    s = to_dev(wl.scores).clone()
+    first, _ = run(topk, wl, scores_dev=s)
+    again, _ = run(topk, wl, scores_dev=s)
+    assert np.array_equal(np.sort(first, 1), np.sort(again, 1))
+    for lens in ([-1, 0, 1, k - 1, k, 32769, 40000, 40017], [40000] * 8, [k + 1] * 8):
+        lens = np.array(lens, np.int32)
+        got, _ = run(topk, wl, scores_dev=s, lengths=lens)
+        assert_parity(wl, got, expect(wl, lengths=lens), lengths=lens)
+    flipped = -wl.scores
+    s.copy_(torch.from_numpy(flipped))
+    fw = synth.Workload("flipped", 27, flipped, wl.lengths, wl.n_cols, k)
+    got, _ = run(topk, fw, scores_dev=s)
+    assert_parity(fw, got, expect(fw))
+
+
+@pytest.mark.parametrize("width", [131072, 262144])
+@pytest.mark.parametrize("k", [512, 2048])
+def test_long_adversarial_rows(topk, width, k):
+    kinds = ["onebin", "crowd16385", "crowd16385_top", "above_fp16", "neginf_few_finite",
+             "signed_zero", "constant", "clustered_peaks", "periodic_peaks", "lowbits10"]
+    wl = synth.mixed_rows(kinds, width, k, seed=28)
+    for force in (0, 3):
+        got, _ = run(topk, wl, force=force)
+        assert_parity(wl, got, expect(wl))

@@ -20,7 +20,7 @@ from topk_check import check, check_fast_raw
 pytestmark = pytest.mark.gpu
 
 GUARD = 4096
-CANARY = 0x5A5A5A5A - 2**32  # as int32
+CANARY = 0x5A5A5A5A
 
 
 @pytest.fixture(scope="session")

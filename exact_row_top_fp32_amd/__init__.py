@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = [
-    "topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity",
+    "topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity", "topk_watchdog_trips",
     "TopKError", "library_path", "PATH_AUTO", "PATH_LDS", "PATH_SAMPLED", "PATH_FULLROW",
     "ROW_EMPTY", "ROW_ALL", "ROW_LDS", "ROW_SAMPLED", "ROW_FULL_OVERFLOW",
     "ROW_FULL_UNDERFLOW", "ROW_FULL_FORCED", "MAX_K",
@@ -61,6 +61,8 @@ def _load():
         lib.topk_status_string.argtypes = [ctypes.c_int]
         lib.topk_max_capacity.restype = ctypes.c_int32
         lib.topk_max_capacity.argtypes = []
+        lib.topk_watchdog_trips.restype = ctypes.c_uint32
+        lib.topk_watchdog_trips.argtypes = []
         _lib = lib
     return _lib
 
@@ -71,6 +73,11 @@ def topk_status_string(status: int) -> str:
 
 def topk_max_capacity() -> int:
     return int(_load().topk_max_capacity())
+
+
+def topk_watchdog_trips() -> int:
+    """Workgroups that gave up a bounded wait since load (nonzero means a defect)."""
+    return int(_load().topk_watchdog_trips())
 
 
 def _device_ptr(t: torch.Tensor | None, name: str, dtype: torch.dtype):

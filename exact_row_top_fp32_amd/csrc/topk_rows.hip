@@ -1,50 +1,67 @@
 // Exact per-row top-k over long, ragged fp32 rows, for gfx950 (CDNA4).
 //
-// One workgroup of 512 lanes (8 wave64s) owns one row. Every comparison is on
-// a uint32 key that orders the float bit patterns by value, so no float
-// compare, rounding or denormal flush is involved anywhere.
+// One persistent launch: one 16-wave workgroup per compute unit, each with
+// two LDS survivor buffers. A workgroup's rows are dealt to it in a fixed
+// order (longest first over the whole batch, dealt out in a snake, so every
+// workgroup gets about the same number of scores) and flow through three
+// roles that hand rows on through LDS progress counters, with no workgroup
+// barrier between rows:
 //
-// Paths inside the one launch (vLLM PR #56346 report, implementation item 1:
-// long and short rows share a launch):
-//  * L <= k: every position is selected.
-//  * L <= capacity: the row is copied into LDS once and selected there.
-//  * longer rows: a uniform sample of contiguous runs gives a cutoff key T
-//    (vLLM PR #56346 report, summary and item 1: sampled cutoff, then exact
-//    selection among survivors); one coalesced pass over the row appends every
-//    key >= T to an LDS survivor buffer with one LDS atomic per wave and step,
-//    counting on past the capacity without writing; the exact cutoff is then
-//    found among the survivors by radix histogram passes.
-//  * survivors > capacity or < m: the full-row path, which finds the exact
-//    cutoff with histogram-only passes over the row and writes the result in
-//    one final pass ("Fix incorrect sparse-attention top-k selection when
-//    candidate bins overflow", comment thread, cutoff-first fallback: refine
-//    with histograms, then one scan writes values above the cutoff and the
-//    cutoff ties into disjoint ranges).
+//  * wave 1 claims rows and estimates each one's cutoff key T from a sample
+//    of the row (vLLM PR #56346 report, summary and implementation item 1: a
+//    sampled cutoff, then exact selection among the survivors);
+//  * waves 2-15 read each row once, in chunks handed out one at a time, with
+//    16-byte buffer loads kept in flight across row boundaries, and append
+//    every key >= T to the row's buffer with one LDS atomic per wave and
+//    chunk, counting on past the capacity without writing, and binning
+//    survivors upward from T as they go (vLLM PR #56346 report,
+//    implementation item 1: ballot hit masks, in-wave prefix sums, one
+//    reservation per wave);
+//  * wave 0 finishes each row once every streaming wave has left it: every
+//    survivor above the cutoff bin is written out and the few in it are
+//    ranked exactly.
 //
-// Every path returns the same set: all positions with key above the cutoff
+// Rows whose survivors overflow the buffer or fall short of k (and rows
+// forced to it) take the full-row path when the queue is done:
+// histogram-only radix passes over the row down to the exact cutoff, then
+// one scan that writes the values above it and the cutoff ties ("Fix
+// incorrect sparse-attention top-k selection when candidate bins overflow",
+// comment thread: cutoff-first fallback; vLLM PR #56346 report,
+// implementation items 1-2: the dual fallback). Rows with L <= k are written
+// out directly.
+//
+// Every path selects the same set: all positions with key above the cutoff
 // key K*, plus the lowest-index positions equal to K* until m are taken.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "exact_topk.h"
+#include <atomic>
 
+#include "exact_topk.h"
+#include "topk_device.h"
+
+namespace topk {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kCapacity = 8192;   // survivor entries held in LDS
-constexpr int kDigitBits = 11;
-constexpr int kBins = 1 << kDigitBits;
-constexpr int kBinsPerLane = kBins / 64;
-constexpr int kUnroll = 4;        // 16-byte loads per lane per streaming step
-constexpr int kRunLen = 64;       // floats per contiguous sample run
-constexpr int kMaxRuns = 64;      // runs per sample (4096 keys at most)
-constexpr int kSampleShift = 10;  // the sample cutoff keeps the top 22 key bits
-constexpr int kMaxCand = 64;      // cutoff-bin entries one wave resolves directly
+constexpr int kThreads = 1024;                            // 16 waves
+constexpr int kFirstStreamer = 2;                          // waves 2..15 stream
+constexpr int kCapacity = 7168;                            // survivor entries per buffer
+constexpr int kUnroll = 4;                                 // 16-byte loads per lane per chunk
+constexpr int kChunkVec = 64 * kUnroll;                    // float4 groups per chunk
+constexpr int kRunLen = 64;                                // floats per contiguous sample run
+constexpr int kMaxRuns = 64;                               // runs per sample
+constexpr int kMaxSample = kMaxRuns * kRunLen;             // 4096 keys at most
+constexpr int kFineShift = 14;                             // T to within 2^14 keys (1/512 octave)
+constexpr int kSlots = 4;                                  // rows i-1 .. i+2
+constexpr int kTable = 64;                                 // queued rows fetched at a time
+constexpr int kMaxDeferred = 64;                           // full-row rows per workgroup
+constexpr int kOrderMaxRows = 2048;                        // longest-first order up to this batch
 
-static_assert(kMaxRuns * kRunLen / 4 <= 2 * kThreads, "two sample loads per lane");
+constexpr uint32_t kKindSampled = 0, kKindAll = 1, kKindFull = 2;
+constexpr uint64_t kWatchdogTicks = 10ull * 100000000ull;  // 10 s
 
-typedef float f4 __attribute__((ext_vector_type(4)));
+__device__ unsigned int g_watchdog_trips;  // workgroups that gave up a wait, since load
 
 struct Params {
     const float* scores;
@@ -59,297 +76,73 @@ struct Params {
     int32_t force_path;
     int32_t capacity;
     int32_t* row_stats;
+    int64_t batch;
+};
+
+struct RowSlot {
+    int64_t b;
+    int64_t L;
+    int64_t nvec;
+    uint32_t m;
+    uint32_t T;
+    uint32_t sh;
+    uint32_t kind;
+    uint32_t valid;
 };
 
 struct Shared {
-    uint32_t key[kCapacity];
-    uint32_t idx[kCapacity];
-    uint32_t hist[kBins];  // all zero between histogram passes
-    uint32_t count;        // survivor slots handed out
-    uint32_t emitted;      // output slots handed out
-    uint32_t found_digit;
-    uint32_t found_above;
-    uint32_t found_count;
-    uint32_t vmin;
-    uint32_t vmax;
-    uint32_t smax;    // largest sample key
-    uint32_t ncand;   // cutoff-bin entries gathered
+    uint32_t key[2][kCapacity];
+    uint32_t idx[2][kCapacity];
+    uint32_t hist[2][kBins];    // survivor histograms, all zero outside a row's use
+    uint32_t skey[kMaxSample];  // the sampler's keys
+    uint32_t shist[kBins];      // the sampler's histogram
+    RowSlot slot[kSlots];
+    uint32_t chunk_next[kSlots];  // next chunk of each slot's row to hand out
+    uint32_t left[kSlots];        // streaming waves done with each slot's row
+    uint32_t n_claimed;           // rows claimed into their slots
+    uint32_t n_ready;             // rows whose cutoff is set
+    uint32_t n_finished;          // rows finished
+    int32_t last_row;             // the row finished by the whole workgroup, or -1
+    uint32_t abort;               // a wait timed out: every role stops
+    uint32_t count[2];            // survivors appended per buffer
+    uint32_t vmax[2];             // largest survivor key per buffer
+    uint32_t found[3];            // finisher's and whole-workgroup selections
+    uint32_t sfound[3];           // sampler's selections
+    uint32_t emitted;             // output slots, finisher and whole workgroup
+    uint32_t semitted;            // output slots, sampler
+    uint32_t ncand;
+    uint32_t smax;
+    uint32_t slo;
     uint32_t cand_key[kMaxCand];
     uint32_t cand_idx[kMaxCand];
+    uint32_t ndeferred;
+    int32_t deferred[kMaxDeferred];
+    int32_t deferred_code[kMaxDeferred];
+    int32_t tab_b[kTable];
+    int32_t tab_len[kTable];
+    uint32_t ndirect;
+    uint32_t tab_n;
+    uint32_t tab_pos;
+    uint32_t tab_round;
+    uint32_t nqueue;   // rows in the order
+    uint32_t ordered;  // the order is longest first, fully tabled at start
 };
 
-// fp32 bits -> uint32 whose unsigned order is the value order: negative
-// patterns are inverted, non-negative ones get the sign bit set. -0 lands just
-// below +0, -inf at the bottom of the finite range, +inf at the top (vLLM PR
-// #56346 report, implementation item 1: a uint32 total-order key).
-__device__ __forceinline__ uint32_t order_key(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+__device__ __forceinline__ int64_t row_len(const Params& p, int64_t b) {
+    int64_t L = p.lengths ? (int64_t)p.lengths[b] : p.n_cols;
+    return L < 0 ? 0 : (L > p.n_cols ? p.n_cols : L);
 }
 
-__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
-
-// number of set bits of `mask` below this lane
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+__device__ __forceinline__ OutRow out_row(const Params& p, int64_t b, uint32_t m, uint32_t* emitted) {
+    return OutRow{p.out + b * (int64_t)p.k, p.page_table ? p.page_table + b * p.pt_stride : nullptr,
+                  p.page_size, m, emitted};
 }
 
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(x, d, 64);
-        if (lane >= (uint32_t)d) x += y;
+__device__ __forceinline__ void put_stats(const Params& p, int64_t b, int code, uint32_t seen) {
+    if (p.row_stats != nullptr) {
+        p.row_stats[2 * b + 0] = code;
+        p.row_stats[2 * b + 1] = (int32_t)seen;
     }
-    return x;
-}
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x = max(x, (uint32_t)__shfl_xor(x, d, 64));
-    return x;
-}
-
-__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x = min(x, (uint32_t)__shfl_xor(x, d, 64));
-    return x;
-}
-
-struct Found {
-    uint32_t digit;  // bin holding the rank-th element from the top
-    uint32_t above;  // elements in higher bins
-    uint32_t count;  // elements in that bin
-};
-
-// Called by every lane after the histogram atomics and a barrier. The first
-// wave finds the bin of the rank-th element from the top: a wave prefix sum
-// over 32-bin groups (lane 0 holding the top group) picks the group, a second
-// one over that group's bins picks the bin. It then zeroes the histogram for
-// the next pass and publishes the bin. 1 <= rank <= histogram total.
-__device__ Found find_rank_bin(Shared& sm, uint32_t rank) {
-    if (threadIdx.x < 64) {
-        const uint32_t lane = threadIdx.x;
-        const uint32_t base = kBins - kBinsPerLane * (lane + 1);
-        uint4* h4 = reinterpret_cast<uint4*>(&sm.hist[base]);
-        uint32_t s = 0;
-#pragma unroll
-        for (int q = 0; q < kBinsPerLane / 4; ++q) {
-            const uint4 v = h4[q];
-            s += v.x + v.y + v.z + v.w;
-        }
-        const uint32_t incl = wave_inclusive_sum(s);
-        const uint64_t own = __ballot(incl - s < rank && rank <= incl);
-        if (own != 0) {
-            const int owner = __ffsll((unsigned long long)own) - 1;
-            const uint32_t obase = kBins - kBinsPerLane * (uint32_t)(owner + 1);
-            const uint32_t oabove = (uint32_t)__builtin_amdgcn_readlane((int)(incl - s), owner);
-            const bool mine = lane < (uint32_t)kBinsPerLane;
-            const uint32_t bin = obase + kBinsPerLane - 1 - (lane & (kBinsPerLane - 1));
-            const uint32_t c = mine ? sm.hist[bin] : 0u;
-            const uint32_t ci = oabove + wave_inclusive_sum(c);
-            if (mine && ci - c < rank && rank <= ci) {
-                sm.found_digit = bin;
-                sm.found_above = ci - c;
-                sm.found_count = c;
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < kBinsPerLane / 4; ++q) h4[q] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    __syncthreads();
-    return Found{sm.found_digit, sm.found_above, sm.found_count};
-}
-
-// ----------------------------------------------------------------------------
-// element sources: the LDS buffer, or the row itself in global memory
-// ----------------------------------------------------------------------------
-
-struct LdsSource {
-    const Shared* sm;
-    uint32_t n;
-    template <class F>
-    __device__ void for_each(F&& f) const {
-        for (uint32_t e = threadIdx.x; e < n; e += kThreads) f(sm->key[e], sm->idx[e]);
-    }
-};
-
-struct RowSource {
-    const float* row;
-    int64_t len;
-    template <class F>
-    __device__ void for_each(F&& f) const {
-        const f4* r4 = reinterpret_cast<const f4*>(row);
-        const int64_t nvec = len >> 2;
-        for (int64_t v = threadIdx.x; v < nvec; v += kThreads) {
-            const f4 x = r4[v];
-            const uint32_t i = (uint32_t)(4 * v);
-            f(order_key(x.x), i);
-            f(order_key(x.y), i + 1);
-            f(order_key(x.z), i + 2);
-            f(order_key(x.w), i + 3);
-        }
-        for (int64_t i = 4 * nvec + threadIdx.x; i < len; i += kThreads) f(order_key(row[i]), (uint32_t)i);
-    }
-};
-
-// value views for selection: the key; the key's top 22 bits; or (among keys
-// equal to `tie`) the inverted index, so that "largest first" means "lowest
-// index first"
-struct KeyView {
-    __device__ bool operator()(uint32_t key, uint32_t, uint32_t& v) const {
-        v = key;
-        return true;
-    }
-};
-struct CoarseKeyView {
-    __device__ bool operator()(uint32_t key, uint32_t, uint32_t& v) const {
-        v = key >> kSampleShift;
-        return true;
-    }
-};
-struct TieIndexView {
-    uint32_t tie;
-    __device__ bool operator()(uint32_t key, uint32_t idx, uint32_t& v) const {
-        v = ~idx;
-        return key == tie;
-    }
-};
-
-template <class Src>
-__device__ void key_range(Shared& sm, const Src& src, uint32_t& vmin, uint32_t& vmax) {
-    if (threadIdx.x == 0) {
-        sm.vmin = 0xFFFFFFFFu;
-        sm.vmax = 0u;
-    }
-    __syncthreads();
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    src.for_each([&](uint32_t key, uint32_t) {
-        lo = min(lo, key);
-        hi = max(hi, key);
-    });
-    lo = wave_min(lo);
-    hi = wave_max(hi);
-    if (lane_id() == 0) {
-        atomicMin(&sm.vmin, lo);
-        atomicMax(&sm.vmax, hi);
-    }
-    __syncthreads();
-    vmin = sm.vmin;
-    vmax = sm.vmax;
-}
-
-struct Cut {
-    uint32_t value;  // exact: the rank-th largest value V*; range: lower edge
-    uint32_t need;   // exact: how many elements equal to V* are in the top rank
-    uint32_t equal;  // exact: how many elements equal V*
-    bool range;      // the top rank are exactly the elements >= value
-};
-
-// Radix selection (vLLM PR #56346 report, implementation item 1: coarse
-// histogram bin, then refinement down to the exact cutoff): the rank-th
-// largest viewed value among the participating elements, whose values all
-// share the bits of `prefix` above bit `nbits`. Histograms of 11-bit digits
-// in LDS, highest digit first; each pass counts only the elements matching
-// the digits chosen so far. When the chosen bin is taken whole, the top rank
-// are exactly the elements at or above its lower edge and the search stops
-// early. 1 <= rank <= number of participating elements.
-template <class Src, class View>
-__device__ Cut radix_select(Shared& sm, const Src& src, View view, uint32_t rank, uint32_t prefix,
-                            int nbits, uint32_t equal_if_none) {
-    Cut cut{prefix, rank, equal_if_none, false};
-    while (nbits > 0) {
-        const int w = nbits < kDigitBits ? nbits : kDigitBits;
-        const int shift = nbits - w;
-        const uint32_t done_mask = nbits >= 32 ? 0u : (0xFFFFFFFFu << nbits);
-        const uint32_t want = prefix & done_mask;
-        const uint32_t dmask = (1u << w) - 1u;
-        src.for_each([&](uint32_t key, uint32_t idx) {
-            uint32_t v;
-            if (view(key, idx, v) && (v & done_mask) == want) atomicAdd(&sm.hist[(v >> shift) & dmask], 1u);
-        });
-        __syncthreads();
-        const Found f = find_rank_bin(sm, rank);
-        rank -= f.above;
-        prefix = want | (f.digit << shift);
-        nbits = shift;
-        cut.equal = f.count;
-        if (nbits > 0 && f.count == rank) {
-            cut.value = prefix;
-            cut.range = true;
-            return cut;
-        }
-    }
-    cut.value = prefix;
-    cut.need = rank;
-    return cut;
-}
-
-// The top m of a source: take key > kth, and key == kth with idx <= icut.
-struct Selection {
-    uint32_t kth;
-    int32_t icut;
-};
-
-__device__ __forceinline__ Selection at_least(uint32_t lo) {
-    return lo == 0u ? Selection{0u, INT32_MAX} : Selection{lo - 1u, -1};
-}
-
-// Exact top m among `src`, whose keys all lie in [lo, hi]; idx < 2^idx_bits.
-template <class Src>
-__device__ Selection select_top(Shared& sm, const Src& src, uint32_t m, uint32_t n, uint32_t lo,
-                                uint32_t hi, int idx_bits) {
-    const int nbits = lo == hi ? 0 : 32 - __clz(lo ^ hi);
-    const Cut c = radix_select(sm, src, KeyView{}, m, lo, nbits, n);
-    if (c.range) return at_least(c.value);
-    Selection s{c.value, INT32_MAX};
-    if (c.need < c.equal) {
-        // the lowest-index ties: the need-th largest inverted index among them;
-        // inverted indices below 2^idx_bits share their top 32 - idx_bits bits
-        const uint32_t iprefix = idx_bits >= 32 ? 0u : (0xFFFFFFFFu << idx_bits);
-        const Cut t = radix_select(sm, src, TieIndexView{c.value}, c.need, iprefix, idx_bits, c.equal);
-        s.icut = (int32_t)(~t.value);  // exact or range: inverted index >= value
-    }
-    return s;
-}
-
-__device__ __forceinline__ int32_t map_slot(const Params& p, int64_t b, uint32_t i) {
-    if (p.page_table == nullptr) return (int32_t)i;
-    const int64_t page = p.page_table[b * p.pt_stride + (int64_t)(i / (uint32_t)p.page_size)];
-    return (int32_t)(page * p.page_size + (int64_t)(i % (uint32_t)p.page_size));
-}
-
-// Slot for every active lane with `pred` from a shared counter: one LDS
-// atomic per wave, lanes ranked by mbcnt over the ballot.
-__device__ __forceinline__ uint32_t wave_reserve(uint32_t* counter, bool pred) {
-    const uint64_t mask = __ballot(pred);
-    uint32_t base = 0u;
-    if (mask != 0) {
-        const int leader = __ffsll((unsigned long long)mask) - 1;
-        if ((int)lane_id() == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-        base = __shfl(base, leader, 64);
-    }
-    return base + lanes_below(mask);
-}
-
-// Appends `idx` (mapped) to the out row for every lane with `take`; slots are
-// handed out by one LDS atomic per wave (ballot + mbcnt). A row's selection
-// holds exactly m elements; the slot bound only keeps a defect from writing
-// outside the row.
-__device__ __forceinline__ void out_append(Shared& sm, bool take, uint32_t idx, uint32_t m, const Params& p,
-                                           int64_t b, int32_t* orow) {
-    const uint32_t slot = wave_reserve(&sm.emitted, take);
-    if (take && slot < m) orow[slot] = map_slot(p, b, idx);
-}
-
-// Writes every selected element of `src` to the out row.
-template <class Src>
-__device__ void emit(Shared& sm, const Src& src, Selection s, uint32_t m, const Params& p, int64_t b,
-                     int32_t* orow) {
-    src.for_each([&](uint32_t key, uint32_t idx) {
-        out_append(sm, key > s.kth || (key == s.kth && (int32_t)idx <= s.icut), idx, m, p, b, orow);
-    });
 }
 
 // Bin of a survivor in the histogram built while streaming: bins of width
@@ -363,326 +156,890 @@ struct StreamBins {
     }
 };
 
-__device__ __forceinline__ f4 load_nt(const f4* p) { return __builtin_nontemporal_load(p); }
+// Position of this workgroup's j-th row in the queue: the order dealt out in
+// a snake (workgroup w takes w, 2G-1-w, 2G+w, ...), pairing long rows with
+// short ones.
+__device__ __forceinline__ uint32_t snake(uint32_t j) {
+    const uint32_t G = gridDim.x;
+    return j * G + ((j & 1u) ? G - 1u - blockIdx.x : blockIdx.x);
+}
 
-// Streaming survivor compaction over the row's float4 groups [0, nvec) with
-// one step of loads always in flight ahead of the step being filtered.
-// `a` holds step 0, already issued by the caller. Hits (key >= T) are
-// appended to the LDS buffer and counted in the survivor histogram; each wave
-// reserves its slots for a step with a single LDS atomic and stops once the
-// running count passes the capacity.
-// kNonNegT: T is the key of a non-negative float, so the test needs only a
-// signed compare of the raw bits.
-template <bool kNonNegT>
-__device__ void stream_steps(Shared& sm, const f4* r4, int64_t nvec, StreamBins bins, uint32_t cap,
-                             f4 (&a)[kUnroll], uint32_t& hmax) {
-    const uint32_t T = bins.T;
-    constexpr int64_t kStep = (int64_t)kThreads * kUnroll;
-    const int32_t Ts = (int32_t)(T ^ 0x80000000u);
+__device__ __forceinline__ uint32_t length_bucket(int64_t L, int64_t n_cols) {
+    return (uint32_t)(L * (kBins - 1) / (n_cols > 0 ? n_cols : 1));
+}
+
+// ----------------------------------------------------------------------------
+// rows selected without a survivor buffer
+// ----------------------------------------------------------------------------
+
+// L <= k: every position, then -1 (an idle row gets only -1). Scope S.
+template <class S>
+__device__ __forceinline__ void direct_row(const Params& p, int64_t b, int64_t L) {
+    const OutRow out = out_row(p, b, (uint32_t)L, nullptr);
+    for (int64_t i = S::rank(); i < p.k; i += S::kSize) out.row[i] = i < L ? out.map((uint32_t)i) : -1;
+    if (S::rank() == 0) put_stats(p, b, L == 0 ? TOPK_ROW_EMPTY : TOPK_ROW_ALL, (uint32_t)L);
+}
+
+// Full-row exact selection of row b by scope S with `hist` all zero.
+template <class S>
+__device__ __forceinline__ void full_row(const Params& p, SelectLds lds, uint32_t* emitted, int64_t b, int code) {
+    const int64_t L = row_len(p, b);
+    const uint32_t m = (uint32_t)(L < p.k ? L : p.k);
+    if (S::rank() == 0) *emitted = 0u;
+    S::sync();
+    const RowSource<S> src{p.scores + b * p.row_stride, L};
+    const Selection s = select_top<S>(lds, src, m, (uint32_t)L, 0u, 0xFFFFFFFFu, bits_for(L));
+    // slots from the LDS counter: the row's loops leave lanes idle at their
+    // ends, so a per-lane counter would fall out of step
+    OutRow out = out_row(p, b, m, emitted);
+    emit(src, s, out);
+    S::sync();
+    if (S::rank() == 0) {
+        put_stats(p, b, code, (uint32_t)L);
+        *emitted = 0u;
+    }
+    S::sync();
+}
+
+// One wave: remember row b for the workgroup's full-row pass; with the list
+// full, select it here with this wave alone, in its own LDS state.
+__device__ __forceinline__ void defer_row(const Params& p, Shared& sm, SelectLds own, uint32_t* own_emitted, int64_t b,
+                          int code) {
+    uint32_t n = 0u;
+    if (lane_id() == 0) n = atomicAdd(&sm.ndeferred, 1u);
+    n = __builtin_amdgcn_readfirstlane(n);
+    if (n < (uint32_t)kMaxDeferred) {
+        if (lane_id() == 0) {
+            sm.deferred[n] = (int32_t)b;
+            sm.deferred_code[n] = code;
+        }
+        WaveScope::sync();
+    } else {
+        full_row<WaveScope>(p, own, own_emitted, b, code);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// the queue
+// ----------------------------------------------------------------------------
+
+// Whole workgroup, at start: rows with L <= k (dealt round-robin) are written
+// out directly. When every workgroup's share fits one table, the other rows
+// are put in a longest-first order (a counting sort over 2048 length buckets,
+// ties by row index, the same in every workgroup) and this workgroup's share
+// of it is tabled; otherwise rows are dealt in index order, a table at a time.
+__device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
+    using B = BlockScope<kThreads>;
+    const int64_t batch = p.batch;
+    const uint32_t G = gridDim.x;
+    if (batch > kOrderMaxRows || batch > (int64_t)kTable * G) {
+        for (int64_t b = blockIdx.x; b < batch; b += G) {
+            const int64_t L = row_len(p, b);
+            if (L <= p.k) direct_row<B>(p, b, L);
+        }
+        if (threadIdx.x == 0) {
+            sm.ordered = 0u;
+            sm.nqueue = (uint32_t)batch;
+            sm.tab_n = (uint32_t)kTable;  // an empty table that asks to be filled
+            sm.tab_pos = (uint32_t)kTable;
+            sm.tab_round = 0u;
+        }
+        B::sync();
+        return;
+    }
+    const uint32_t n = (uint32_t)batch;
+    uint32_t* bucket = sm.key[0];  // per row: its length bucket, kBins for L <= k
+    int32_t* len = reinterpret_cast<int32_t*>(sm.idx[0]);
+    uint32_t* placed = sm.key[1];  // rows by bucket, any order within one
+    uint32_t* order = sm.idx[1];   // rows by bucket, index order within one
+    uint32_t* direct = sm.skey;    // this workgroup's rows with L <= k
+    uint32_t* cnt = sm.hist[0];
+    uint32_t* start = sm.hist[1];  // rows in higher buckets
+    uint32_t* fill = sm.shist;
+    for (uint32_t b = threadIdx.x; b < n; b += kThreads) {
+        const int64_t L = row_len(p, b);
+        len[b] = (int32_t)L;
+        uint32_t d = (uint32_t)kBins;
+        if (L > p.k) {
+            d = length_bucket(L, p.n_cols);
+            atomicAdd(&cnt[d], 1u);
+        } else if (b % G == blockIdx.x) {
+            direct[atomicAdd(&sm.ndirect, 1u)] = b;
+        }
+        bucket[b] = d;
+    }
+    B::sync();
+    if (threadIdx.x < 64) {  // suffix sums of the bucket counts, 32 buckets per lane
+        const uint32_t lane = lane_id();
+        const uint32_t* c = cnt + 32 * lane;
+        uint32_t own = 0;
+        for (int j = 0; j < 32; ++j) own += c[j];
+        const uint32_t incl = wave_inclusive_sum(own);
+        const uint32_t total = __shfl(incl, 63, 64);
+        uint32_t above = total - incl;  // rows in the buckets of higher lanes
+        for (int j = 31; j >= 0; --j) {
+            start[32 * lane + j] = above;
+            above += c[j];
+        }
+        if (lane == 0) sm.nqueue = total;
+    }
+    B::sync();
+    for (uint32_t b = threadIdx.x; b < n; b += kThreads) {
+        const uint32_t d = bucket[b];
+        if (d < (uint32_t)kBins) placed[start[d] + atomicAdd(&fill[d], 1u)] = b;
+    }
+    B::sync();
+    const uint32_t total = sm.nqueue;
+    for (uint32_t t = threadIdx.x; t < total; t += kThreads) {
+        const uint32_t b = placed[t];
+        const uint32_t d = bucket[b];
+        const uint32_t s0 = start[d], s1 = s0 + cnt[d];
+        uint32_t r = 0;
+        for (uint32_t u = s0; u < s1; ++u) r += placed[u] < b ? 1u : 0u;
+        order[s0 + r] = b;
+    }
+    B::sync();
+    if (threadIdx.x < 64) {
+        const uint32_t j = lane_id();
+        const uint32_t t = snake(j);  // grows with j, so the valid entries lead
+        const bool ok = t < total;
+        if (ok) {
+            const uint32_t b = order[t];
+            sm.tab_b[j] = (int32_t)b;
+            sm.tab_len[j] = len[b];
+        }
+        const uint32_t nt = (uint32_t)__popcll(__ballot(ok));
+        if (j == 0) {
+            sm.ordered = 1u;
+            sm.tab_n = nt;
+            sm.tab_pos = 0u;
+            sm.tab_round = 0u;
+        }
+    }
+    const uint32_t nd = sm.ndirect;
+    B::sync();
+    for (int i = threadIdx.x; i < kBins; i += kThreads) cnt[i] = start[i] = fill[i] = 0u;
+    for (uint32_t j = 0; j < nd; ++j) {
+        const uint32_t b = direct[j];
+        direct_row<B>(p, b, len[b]);
+    }
+    B::sync();
+}
+
+// One wave: the next kTable rows of this workgroup in index order.
+__device__ __forceinline__ void fill_table(const Params& p, Shared& sm) {
     const uint32_t lane = lane_id();
-    auto hit = [&](float x) -> bool {
-        if constexpr (kNonNegT) return (int32_t)__float_as_uint(x) >= Ts;
-        else return order_key(x) >= T;
-    };
-    auto load = [&](f4 (&x)[kUnroll], int64_t v0) {
+    const uint32_t t = snake(sm.tab_round + lane);
+    const bool ok = t < sm.nqueue;
+    const uint32_t n = (uint32_t)__popcll(__ballot(ok));  // snake() grows, so the valid ones lead
+    if (ok) {
+        sm.tab_b[lane] = (int32_t)t;
+        sm.tab_len[lane] = (int32_t)row_len(p, t);
+    }
+    WaveScope::sync();
+    if (lane == 0) {
+        sm.tab_n = n;
+        sm.tab_pos = 0u;
+        sm.tab_round += kTable;
+    }
+    WaveScope::sync();
+}
+
+// One wave: this workgroup's next row into `slot` (invalid once its share is
+// done). Rows with L <= k were written at start; rows forced to the full-row
+// path are deferred on the way. The cutoff of a sampled row is set later.
+__device__ __forceinline__ void claim_row(const Params& p, Shared& sm, RowSlot& slot, SelectLds own, uint32_t* own_emitted) {
+    for (;;) {
+        if (sm.tab_pos == sm.tab_n) {
+            if (sm.ordered || sm.tab_n < (uint32_t)kTable) {
+                if (lane_id() == 0) slot.valid = 0u;
+                break;
+            }
+            fill_table(p, sm);
+            continue;
+        }
+        const int64_t b = sm.tab_b[sm.tab_pos];
+        const int64_t L = sm.tab_len[sm.tab_pos];
+        WaveScope::sync();
+        if (lane_id() == 0) sm.tab_pos += 1u;
+        WaveScope::sync();
+        if (L <= p.k) continue;
+        const int64_t cap = p.capacity;
+        uint32_t kind;
+        if (p.force_path == TOPK_PATH_FULLROW || (p.force_path == TOPK_PATH_LDS && L > cap)) kind = kKindFull;
+        else if (p.force_path == TOPK_PATH_LDS || (p.force_path == TOPK_PATH_AUTO && L <= cap)) kind = kKindAll;
+        else kind = kKindSampled;
+        if (kind == kKindFull) {
+            defer_row(p, sm, own, own_emitted, b, TOPK_ROW_FULL_FORCED);
+            continue;
+        }
+        if (lane_id() == 0) {
+            slot.b = b;
+            slot.L = L;
+            slot.nvec = L >> 2;
+            slot.m = (uint32_t)p.k;
+            slot.T = 0u;                     // kKindAll: every key survives
+            slot.sh = 32 - kDigitBits;       // and bins take the top 11 bits
+            slot.kind = kind;
+            slot.valid = 1u;
+        }
+        break;
+    }
+    WaveScope::sync();
+}
+
+// Scope S: the cutoff of a sampled row. A sample of `runs` runs of 64
+// contiguous scores spread evenly over [0, L) gives T at or just below the
+// want-th largest sample key, want set so that the expected survivor count
+// sits several standard deviations above m (the number of sample keys above
+// the true m-th key is binomial).
+//
+// The sample goes straight from HBM to LDS (every load in flight at once, no
+// registers held). Each lane then keeps its q = ceil(want / lanes) largest
+// keys; the smallest of the lanes' q-th largest, lo, has at least want keys
+// at or above it (lo = 0 when q is too large to keep). A histogram of the
+// keys in [lo, sample max], in 2048 bins, locates the want-th largest; its
+// bin is narrowed by further histograms until bins are at most 2^kFineShift
+// keys wide, and T is the lower edge of the last bin. The bin width of the
+// survivor histogram makes [T, sample max] cover about half its bins.
+template <class S>
+__device__ __forceinline__ void sample_cutoff(const Params& p, Shared& sm, RowSlot& R, SelectLds lds) {
+    constexpr int kPer = (kMaxSample / 4 + S::kSize - 1) / S::kSize;  // 16-byte loads per lane
+    constexpr int kQ = 4;                                              // most keys kept per lane
+    const int64_t L = R.L;
+    const float* row = p.scores + R.b * p.row_stride;
+    const int64_t fit = L / (2 * kRunLen);
+    const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
+    constexpr int kVecPerRun = kRunLen / 4;
+    const int nsv = runs >= 2 ? runs * kVecPerRun : 0;
+    // run r starts at floor(r * (L - 64) / (runs - 1)), rounded down to 4
+    const int64_t span_runs = runs >= 2 ? (L - kRunLen) : 0;
+    const int64_t step_q = runs >= 2 ? span_runs / (runs - 1) : 0;
+    const uint32_t step_r = runs >= 2 ? (uint32_t)(span_runs - step_q * (runs - 1)) : 0u;
+    const uint32_t n = (uint32_t)nsv * 4;
+    const float mu = (float)R.m * (float)n / (float)L;
+    const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
+    const uint32_t want = wantf < (float)n ? (uint32_t)wantf : 0u;  // 0: keep every key
+    const uint32_t q = (want + S::kSize - 1) / S::kSize;
+    // lane l of a wave writes 16 bytes at the wave's LDS base + 16 l, so
+    // group t (4 scores) lands at skey[4t, 4t + 4)
+    const uint32_t wave_base = S::rank() & ~63u;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t v = v0 + u * kThreads + threadIdx.x;
-            x[u] = v < nvec ? load_nt(r4 + v) : f4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < kPer; ++h) {
+        const int t = h * S::kSize + (int)S::rank();
+        if (t < nsv) {
+            const int r = t / kVecPerRun;
+            const int64_t start =
+                ((int64_t)r * step_q + (int64_t)(((uint32_t)r * step_r) / (uint32_t)(runs - 1))) & ~(int64_t)3;
+            __builtin_amdgcn_global_load_lds(
+                row + start + 4 * (t % kVecPerRun),
+                (__attribute__((address_space(3))) void*)(sm.skey + 4 * (h * S::kSize + wave_base)), 16, 0, 0);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // each lane reads back only the groups its own loads wrote
+    auto each_key = [&](auto&& f) {
+#pragma unroll 4
+        for (int h = 0; h < kPer; ++h) {
+            const int t = h * S::kSize + (int)S::rank();
+            if (t < nsv) {
+                const uint4 g = *reinterpret_cast<const uint4*>(sm.skey + 4 * t);
+                f(order_key(__uint_as_float(g.x)));
+                f(order_key(__uint_as_float(g.y)));
+                f(order_key(__uint_as_float(g.z)));
+                f(order_key(__uint_as_float(g.w)));
+            }
         }
     };
-    // false once the running count has passed the capacity
-    auto filter = [&](const f4 (&x)[kUnroll], int64_t v0) -> bool {
+    uint32_t top[kQ] = {0u, 0u, 0u, 0u};  // this lane's largest keys, descending
+    uint32_t smax = 0u;
+    each_key([&](uint32_t key) {
+        smax = max(smax, key);
+#pragma unroll
+        for (int j = 0; j < kQ; ++j) {
+            const uint32_t hi = max(top[j], key);
+            key = min(top[j], key);
+            top[j] = hi;
+        }
+    });
+    uint32_t lo = 0u;
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) lo = (uint32_t)(j + 1) == q ? top[j] : lo;
+    lo = wave_min(lo);
+    smax = wave_max(smax);
+    if (S::rank() == 0) {
+        sm.smax = 0u;
+        sm.slo = 0xFFFFFFFFu;
+    }
+    S::sync();
+    if (lane_id() == 0) {
+        atomicMax(&sm.smax, smax);
+        atomicMin(&sm.slo, lo);
+    }
+    S::sync();
+    const uint32_t hi = sm.smax;
+    lo = sm.slo;
+    uint32_t T = 0u;  // too short to sample, or want out of reach: keep everything
+    if (want > 0) {
+        // the rank-th largest key in [base, top] lies in one of 2048 bins of
+        // width 2^sh; narrow to that bin until bins are fine enough
+        uint32_t base = q > (uint32_t)kQ ? 0u : lo, top = hi, rank = want;
+        for (;;) {
+            const uint32_t span = top - base;
+            const int wb = span == 0u ? 0 : 32 - __clz(span);
+            const int sh = wb > kDigitBits ? wb - kDigitBits : 0;  // span >> sh < 2048
+            each_key([&](uint32_t key) {
+                if (key >= base && key <= top) atomicAdd(&lds.hist[(key - base) >> sh], 1u);
+            });
+            S::sync();
+            const Found f = find_rank_bin<S>(lds, rank);
+            const uint32_t edge = base + (f.digit << sh);
+            if (sh <= kFineShift) {
+                T = edge;
+                break;
+            }
+            rank -= f.above;
+            const uint32_t room = top - edge;
+            top = edge + (room < (1u << sh) - 1u ? room : (1u << sh) - 1u);
+            base = edge;
+        }
+    }
+    const uint32_t span = hi - T;
+    const int wbits = span == 0u ? 0 : 32 - __clz(span);
+    if (S::rank() == 0) {
+        R.T = T;
+        R.sh = (uint32_t)(wbits > kDigitBits - 1 ? wbits - (kDigitBits - 1) : 0);
+    }
+    S::sync();
+}
+
+// ----------------------------------------------------------------------------
+// progress counters between the roles
+// ----------------------------------------------------------------------------
+//
+// Rows go through the workgroup in sequence i = 0, 1, ...: row i sits in slot
+// i % kSlots and its survivors in buffer i % 2. The sampler wave claims rows
+// (n_claimed) and sets their cutoffs (n_ready); the finisher wave finishes
+// them (n_finished) once every streaming wave has left them (left[slot]). A
+// streaming wave reads chunks of a claimed row, filters them once the row's
+// cutoff is set and its buffer free (row i - 2 finished), and leaves the row
+// after its last chunk of it. Every wait is on an earlier row, or on a row
+// the waiting wave holds nothing of, so none can close a cycle.
+
+// Counters are written by one lane after the wave's earlier LDS writes are
+// done, and read by every lane of the waiting wave.
+__device__ __forceinline__ void publish(uint32_t* ctr, uint32_t v) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane_id() == 0) __hip_atomic_store(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void publish_add(uint32_t* ctr, uint32_t v) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane_id() == 0) __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ uint32_t peek(const uint32_t* ctr) {
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+
+// Waits until *ctr >= v; false if the workgroup gave up instead. A wait that
+// outlasts kWatchdogTicks of the 100 MHz wall clock (far beyond any row the
+// API admits) gives the workgroup up, so that a defect ends the launch rather
+// than hanging it, and counts a trip in g_watchdog_trips.
+__device__ __forceinline__ bool wait_for(Shared& sm, const uint32_t* ctr, uint32_t v) {
+    uint64_t t0 = 0;
+    for (uint32_t n = 0;; ++n) {
+        if (peek(ctr) >= v) {
+            asm volatile("" ::: "memory");
+            return true;
+        }
+        if (peek(&sm.abort) != 0u) return false;
+        if ((n & 1023u) == 0u) {
+            const uint64_t t = wall_clock64();
+            if (n == 0u) {
+                t0 = t;
+            } else if (t - t0 > kWatchdogTicks) {
+                if (lane_id() == 0) sm.abort = 1u;
+                return false;
+            }
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// streaming
+// ----------------------------------------------------------------------------
+
+constexpr int kStreamers = kThreads / 64 - kFirstStreamer;
+constexpr uint32_t kNone = 0xFFFFFFFEu;  // no chunk within reach
+constexpr uint32_t kEnd = 0xFFFFFFFFu;   // this workgroup's rows are done
+
+// Streaming waves read a row's full groups of 4 scores in chunks of
+// kChunkVec groups; the finisher takes the last L % 4 scores.
+__device__ __forceinline__ uint32_t nchunks(const RowSlot& R) {
+    const int64_t groups = R.L >> 2;
+    return (uint32_t)((groups + kChunkVec - 1) / kChunkVec);
+}
+
+// A chunk in registers: kUnroll groups of 4 scores per lane.
+struct Chunk {
+    f4 v[kUnroll];
+};
+
+constexpr uint32_t kBufferConfig = 0x00020000u;  // raw buffer descriptor word 3 on CDNA
+constexpr int kNonTemporal = 2;                  // buffer load cache policy: streaming
+
+__device__ __forceinline__ uint64_t uniform(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Issues the loads of chunk c (full groups only) of a row of L scores;
+// c >= kNone issues loads that touch no memory. Every call issues the same
+// kUnroll buffer loads, so the count of loads in flight never depends on the
+// path taken; loads past the descriptor's range return zero without a
+// memory access.
+__device__ __forceinline__ void load_chunk(Chunk& x, const float* row, int64_t L, uint32_t c) {
+    const uint32_t lane = lane_id();
+    L = (int64_t)uniform((uint64_t)L);
+    const uint64_t rowp = uniform((uint64_t)reinterpret_cast<uintptr_t>(row));
+    const int64_t g0 = c < kNone ? (int64_t)c * kChunkVec : 0;  // first group of the chunk
+    int64_t nf = c < kNone ? (L >> 2) - g0 : 0;                  // full groups in it
+    nf = nf < 0 ? 0 : (nf > kChunkVec ? kChunkVec : nf);
+    const __amdgpu_buffer_rsrc_t body = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(rowp + 16u * (uint64_t)g0), 0, (int)(16 * nf), (int)kBufferConfig);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(body, (int)(16 * (lane + 64 * u)), 0, kNonTemporal);
+        x.v[u] = f4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])};
+    }
+}
+
+// The last L % 4 scores of a row, one per lane of the finisher wave, which
+// appends their hits to the row's buffer as a streaming wave would. The
+// buffer is free by then, and appends from several waves may interleave.
+__device__ __forceinline__ float load_tail(const Params& p, const RowSlot& R) {
+    const uint32_t lane = lane_id();
+    return lane < (uint32_t)(R.L & 3) ? p.scores[R.b * p.row_stride + (R.L & ~(int64_t)3) + lane] : 0.f;
+}
+
+__device__ __forceinline__ void append_tail(Shared& sm, const RowSlot& R, int x, uint32_t cap, float t) {
+    const uint32_t lane = lane_id();
+    const uint32_t kk = order_key(t);
+    const bool h = lane < (uint32_t)(R.L & 3) && kk >= R.T;
+    const uint64_t mk = __ballot(h);
+    if (mk != 0) {
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&sm.count[x], (uint32_t)__popcll(mk));
+        base = __builtin_amdgcn_readfirstlane(base);
+        const uint32_t pos = base + lanes_below(mk);
+        if (h && pos < cap) {
+            sm.key[x][pos] = kk;
+            sm.idx[x][pos] = (uint32_t)(R.L & ~(int64_t)3) + lane;
+            atomicAdd(&sm.hist[x][StreamBins{R.T, R.sh}(kk)], 1u);
+        }
+        const uint32_t h_max = wave_max(h ? kk : 0u);
+        if (lane == 0) atomicMax(&sm.vmax[x], h_max);
+    }
+    WaveScope::sync();
+}
+
+// One streaming wave.
+struct Streamer {
+    const Params& p;
+    Shared& sm;
+    uint32_t cap;
+    int i;       // row of the chunk held
+    uint32_t c;  // the chunk held
+    int open;    // the row whose filter state below is loaded, or -1
+    int ok;      // rows up to this one have their cutoff set and their buffer free
+    uint32_t T, sh, buf, hmax;
+    int64_t L;
+
+    __device__ __forceinline__ void leave(int r) { publish_add(&sm.left[r % kSlots], 1u); }
+
+    // The next chunk at or after row r (the row of the chunk held, if
+    // `holding`), waiting for rows to be claimed only up to row lim. Rows
+    // passed on the way are left, except r while a chunk of it is held.
+    // Returns the chunk with r set to its row; kNone with r the first row not
+    // looked at; kEnd past this workgroup's last row.
+    __device__ __forceinline__ uint32_t grab(int& r, int lim, bool holding) {
+        for (;;) {
+            if (r > lim) return kNone;
+            if (!wait_for(sm, &sm.n_claimed, (uint32_t)r + 1u)) return kEnd;
+            const RowSlot& R = sm.slot[r % kSlots];
+            if (!R.valid) return kEnd;
+            uint32_t ch = 0u;
+            if (lane_id() == 0) ch = atomicAdd(&sm.chunk_next[r % kSlots], 1u);
+            ch = __builtin_amdgcn_readfirstlane(ch);
+            if (ch < nchunks(R)) return ch;
+            if (!holding) leave(r);
+            holding = false;
+            ++r;
+        }
+    }
+
+    __device__ __forceinline__ void load(Chunk& v, int r, uint32_t ch) {
+        const RowSlot& R = sm.slot[r % kSlots];
+        load_chunk(v, p.scores + R.b * p.row_stride, R.L, ch);
+    }
+
+    // Appends the hits of chunk ch of row r (key >= T) to the row's buffer
+    // with one LDS atomic, and bins them; false once the row's count has
+    // passed the capacity. kNonNegT: T is the key of a non-negative float,
+    // so a signed compare of the raw bits decides.
+    template <bool kNonNegT>
+    __device__ __forceinline__ bool filter(const Chunk& x, uint32_t ch) {
+        const uint32_t lane = lane_id();
+        const int64_t v0 = (int64_t)ch * kChunkVec + lane;
+        const int32_t Ts = (int32_t)(T ^ 0x80000000u);
+        const StreamBins bins{T, sh};
+        uint32_t* key = sm.key[buf];
+        uint32_t* idx = sm.idx[buf];
+        uint32_t* hist = sm.hist[buf];
+        auto hit = [&](float f) -> bool {
+            if constexpr (kNonNegT) return (int32_t)__float_as_uint(f) >= Ts;
+            else return order_key(f) >= T;
+        };
+        const int64_t nfull = L >> 2;
+        const f4 (&v)[kUnroll] = x.v;
         uint64_t masks[4 * kUnroll];
         uint32_t total = 0;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const bool ok = v0 + u * kThreads + threadIdx.x < nvec;
+            const bool ok = v0 + u * 64 < nfull;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                masks[4 * u + c] = __ballot(ok && hit(x[u][c]));
-                total += (uint32_t)__popcll(masks[4 * u + c]);
+            for (int e = 0; e < 4; ++e) {
+                masks[4 * u + e] = __ballot(ok && hit(v[u][e]));
+                total += (uint32_t)__popcll(masks[4 * u + e]);
             }
         }
         if (total == 0) return true;
         uint32_t base = 0u;
-        if (lane == 0) base = atomicAdd(&sm.count, total);
+        if (lane == 0) base = atomicAdd(&sm.count[buf], total);
         base = __builtin_amdgcn_readfirstlane(base);
         if (base >= cap) return false;
         uint32_t off = base;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t i0 = (uint32_t)(4 * (v0 + u * kThreads + threadIdx.x));
+            const uint32_t i0 = (uint32_t)(4 * (v0 + u * 64));
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint64_t mk = masks[4 * u + c];
+            for (int e = 0; e < 4; ++e) {
+                const uint64_t mk = masks[4 * u + e];
                 if ((mk >> lane) & 1u) {
                     const uint32_t pos = off + lanes_below(mk);
-                    const uint32_t key = order_key(x[u][c]);
-                    hmax = max(hmax, key);
+                    const uint32_t kk = order_key(v[u][e]);
+                    hmax = max(hmax, kk);
                     if (pos < cap) {
-                        sm.key[pos] = key;
-                        sm.idx[pos] = i0 + (uint32_t)c;
-                        atomicAdd(&sm.hist[bins(key)], 1u);
+                        key[pos] = kk;
+                        idx[pos] = i0 + (uint32_t)e;
+                        atomicAdd(&hist[bins(kk)], 1u);
                     }
                 }
                 off += (uint32_t)__popcll(mk);
             }
         }
         return base + total <= cap;
-    };
-    f4 b[kUnroll];
-    int64_t v0 = 0;
-    while (v0 < nvec) {
-        load(b, v0 + kStep);
-        if (!filter(a, v0)) break;
-        v0 += kStep;
-        if (v0 >= nvec) break;
-        load(a, v0 + kStep);
-        if (!filter(b, v0)) break;
-        v0 += kStep;
     }
-}
 
-// Sampled path for a row with L > k: returns the survivor count n (n > cap
-// means the buffer overflowed and holds an arbitrary subset). On return the
-// buffer holds the survivors, [bins.T, vmax] bounds their keys, and the
-// histogram counts them by bins(key) (unless the buffer overflowed).
-//
-// The cutoff T comes from a sample of `runs` runs of 64 contiguous scores
-// spread evenly over [0, L): the lower edge of the 22-bit key bucket holding
-// the rank-th largest sample key, the rank chosen so that the expected
-// survivor count sits several standard deviations above m (the number of
-// sample keys above the true m-th key is binomial).
-__device__ uint32_t sampled_survivors(Shared& sm, const float* row, int64_t L, uint32_t m, uint32_t cap,
-                                      StreamBins& bins, uint32_t& vmax) {
-    const f4* r4 = reinterpret_cast<const f4*>(row);
-    const int64_t nvec = L >> 2;
-    const int64_t fit = L / (2 * kRunLen);
-    const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
-    constexpr int kVecPerRun = kRunLen / 4;
-    const int nsv = runs >= 2 ? runs * kVecPerRun : 0;
-
-    // sample loads first, then step 0 of the stream, all in flight together
-    f4 sv[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int t = threadIdx.x + h * kThreads;
-        if (t < nsv) {
-            const int r = t / kVecPerRun;
-            const int64_t start = ((int64_t)r * (L - kRunLen) / (runs - 1)) & ~(int64_t)3;
-            sv[h] = r4[start / 4 + t % kVecPerRun];
+    __device__ __forceinline__ bool filter_held(const Chunk& v) {
+        if (i != open) {
+            if (i > ok) {
+                if (!wait_for(sm, &sm.n_ready, (uint32_t)i + 1u)) return false;
+                if (i >= 2 && !wait_for(sm, &sm.n_finished, (uint32_t)i - 1u)) return false;
+                ok = i;
+            }
+            const RowSlot& R = sm.slot[i % kSlots];
+            T = R.T;
+            sh = R.sh;
+            L = R.L;
+            buf = (uint32_t)(i & 1);
+            open = i;
         }
+        return T >= 0x80000000u ? filter<true>(v, c) : filter<false>(v, c);
     }
-    f4 a[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int64_t v = u * kThreads + threadIdx.x;
-        a[u] = v < nvec ? load_nt(r4 + v) : f4{0.f, 0.f, 0.f, 0.f};
+
+    // Done with row r: its largest survivor key, then the count of waves out.
+    __device__ __forceinline__ void close(int r) {
+        const uint32_t h = wave_max(hmax);
+        if (lane_id() == 0 && h != 0u) atomicMax(&sm.vmax[r & 1], h);
+        hmax = 0u;
+        leave(r);
     }
-    uint32_t smax = 0u;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int t = threadIdx.x + h * kThreads;
-        if (t < nsv) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t key = order_key(sv[h][c]);
-                sm.key[4 * t + c] = key;
-                smax = max(smax, key);
+
+    // Holding chunk c of row i in `held`: issue the next chunk into `next`,
+    // then filter `held`. False when this workgroup's rows are done.
+    __device__ __forceinline__ bool step(Chunk& held, Chunk& next) {
+        int r = i;
+        uint32_t cn = grab(r, i + 2, true);
+        load(next, r, cn);
+        if (!filter_held(held)) {
+            // over capacity: no wave takes more of this row
+            if (lane_id() == 0) atomicMax(&sm.chunk_next[i % kSlots], nchunks(sm.slot[i % kSlots]));
+            if (r == i) {  // drop the chunk just issued
+                r = i + 1;
+                cn = kNone;
             }
         }
-    }
-    smax = wave_max(smax);
-    if (lane_id() == 0) atomicMax(&sm.smax, smax);
-    __syncthreads();
-
-    uint32_t T = 0u;  // too short to sample: keep everything
-    if (nsv > 0) {
-        const uint32_t S = (uint32_t)nsv * 4;
-        const float mu = (float)m * (float)S / (float)L;
-        const float want = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
-        if (want < (float)S) {
-            const Cut c = radix_select(sm, LdsSource{&sm, S}, CoarseKeyView{}, (uint32_t)want, 0u,
-                                       32 - kSampleShift, S);
-            T = c.value << kSampleShift;
+        if (r != i) close(i);
+        if (cn == kNone) {  // nothing held now, so waiting for any row is safe
+            cn = grab(r, INT32_MAX, false);
+            if (cn < kNone) load(next, r, cn);
         }
+        if (cn == kEnd) return false;
+        i = r;
+        c = cn;
+        return true;
     }
+};
 
-    // survivor histogram: the span [T, sample max] covers about half the bins
-    const uint32_t span = sm.smax - T;
-    const int wbits = span == 0u ? 0 : 32 - __clz(span);
-    bins = StreamBins{T, (uint32_t)(wbits > kDigitBits - 1 ? wbits - (kDigitBits - 1) : 0)};
+// ----------------------------------------------------------------------------
+// finishing a row from its survivors
+// ----------------------------------------------------------------------------
 
-    uint32_t hmax = 0u;
-    if (T >= 0x80000000u) stream_steps<true>(sm, r4, nvec, bins, cap, a, hmax);
-    else stream_steps<false>(sm, r4, nvec, bins, cap, a, hmax);
-
-    // the last L % 4 positions, by the first wave
-    if (threadIdx.x < 64) {
-        const int64_t i = 4 * nvec + lane_id();
-        const uint32_t key = i < L ? order_key(row[i]) : 0u;
-        const bool hit = i < L && key >= T;
-        const uint64_t mk = __ballot(hit);
-        if (mk != 0) {
-            uint32_t base = 0u;
-            if (lane_id() == 0) base = atomicAdd(&sm.count, (uint32_t)__popcll(mk));
-            base = __builtin_amdgcn_readfirstlane(base);
-            if (hit) {
-                const uint32_t pos = base + lanes_below(mk);
-                hmax = max(hmax, key);
-                if (pos < cap) {
-                    sm.key[pos] = key;
-                    sm.idx[pos] = (uint32_t)i;
-                    atomicAdd(&sm.hist[bins(key)], 1u);
+// Scope S (wave 0 alone, or the whole workgroup for the last row): the exact
+// top m of row R from the n survivors in buffer x, using the histogram built
+// while streaming. Every survivor in a bin above the cutoff bin is written
+// out in one pass over the buffer, which also gathers the cutoff bin's
+// entries; one wave ranks those by (key descending, index ascending) and
+// writes the first `need`. A crowded or open-ended cutoff bin takes the radix
+// select over the buffer instead. Leaves buffer x's counters and histogram zero.
+template <class S>
+__device__ __forceinline__ void finish_row(const Params& p, Shared& sm, const RowSlot& R, int x, uint32_t cap) {
+    constexpr bool kWave = S::kSize == 64;
+    const uint32_t n = sm.count[x];
+    const uint32_t m = R.m;
+    uint32_t* hist = sm.hist[x];
+    const SelectLds lds{hist, sm.found};
+    if (n > cap || n < m) {
+        for (int i = S::rank(); i < kBins; i += S::kSize) hist[i] = 0u;
+        S::sync();
+        const int code = n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
+        if (S::first_wave()) defer_row(p, sm, lds, &sm.emitted, R.b, code);
+    } else {
+        const StreamBins bins{R.T, R.sh};
+        const Found f = find_rank_bin<S>(lds, m);
+        if (f.count > (uint32_t)kMaxCand || f.digit == (uint32_t)kBins - 1u) {
+            const LdsSource<S> src{sm.key[x], sm.idx[x], n};
+            const Selection s = select_top<S>(lds, src, m, n, R.T, sm.vmax[x], bits_for(R.L));
+            OutRow out = out_row(p, R.b, m, &sm.emitted);
+            emit(src, s, out);
+        } else {
+            const uint32_t d = f.digit;
+            const uint32_t need = m - f.above;
+            const bool whole = f.count == need;  // the cutoff bin is taken whole
+            const uint32_t* K = sm.key[x];
+            const uint32_t* I = sm.idx[x];
+            if constexpr (kWave) {
+                // every lane runs every iteration, so per-lane slot counters
+                // stay in step across the wave
+                const uint32_t lane = lane_id();
+                WaveOutRow out{out_row(p, R.b, m, nullptr), 0u};
+                uint32_t ncand = 0u;
+                for (uint32_t e0 = 0; e0 < n; e0 += 4 * 64) {
+                    uint32_t kk[4], ii[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t e = e0 + 64 * j + lane;
+                        kk[j] = e < n ? K[e] : 0u;
+                        ii[j] = e < n ? I[e] : 0u;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool ok = e0 + 64 * j + lane < n;
+                        const uint32_t bk = bins(kk[j]);
+                        out.append(ok && (bk > d || (whole && bk == d)), ii[j]);
+                        const bool cand = ok && !whole && bk == d;
+                        const uint64_t cm = __ballot(cand);
+                        if (cand) {
+                            const uint32_t slot = ncand + lanes_below(cm);
+                            if (slot < (uint32_t)kMaxCand) {
+                                sm.cand_key[slot] = kk[j];
+                                sm.cand_idx[slot] = ii[j];
+                            }
+                        }
+                        ncand += (uint32_t)__popcll(cm);
+                    }
+                }
+                if (!whole) {
+                    S::sync();
+                    const uint32_t nc = f.count;
+                    const bool have = lane < nc;
+                    const uint32_t kj = have ? sm.cand_key[lane] : 0u;
+                    const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
+                    uint32_t r = 0;  // candidates ranked before this one
+                    for (uint32_t i = 0; i < nc; ++i) {
+                        const uint32_t ki = sm.cand_key[i];
+                        const uint32_t ii = sm.cand_idx[i];
+                        r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
+                    }
+                    out.append(have && r < need, ij);
+                }
+            } else {
+                OutRow out = out_row(p, R.b, m, &sm.emitted);
+                for (uint32_t e = S::rank(); e < n; e += S::kSize) {
+                    const uint32_t kk = K[e], ii = I[e];
+                    const uint32_t bk = bins(kk);
+                    out.append(bk > d || (whole && bk == d), ii);
+                    const bool cand = !whole && bk == d;
+                    const uint32_t slot = wave_reserve(&sm.ncand, cand);
+                    if (cand && slot < (uint32_t)kMaxCand) {
+                        sm.cand_key[slot] = kk;
+                        sm.cand_idx[slot] = ii;
+                    }
+                }
+                S::sync();
+                if (!whole && S::first_wave()) {
+                    const uint32_t lane = lane_id();
+                    const uint32_t nc = f.count;
+                    const bool have = lane < nc;
+                    const uint32_t kj = have ? sm.cand_key[lane] : 0u;
+                    const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
+                    uint32_t r = 0;
+                    for (uint32_t i = 0; i < nc; ++i) {
+                        const uint32_t ki = sm.cand_key[i];
+                        const uint32_t ii = sm.cand_idx[i];
+                        r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
+                    }
+                    out.append(have && r < need, ij);
                 }
             }
         }
+        if (S::rank() == 0) put_stats(p, R.b, R.kind == kKindAll ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED, n);
     }
-    hmax = wave_max(hmax);
-    if (lane_id() == 0) atomicMax(&sm.vmax, hmax);
-    __syncthreads();
-    vmax = sm.vmax;
-    return sm.count;
-}
-
-// Exact top m of the n >= m survivors, from the histogram built while
-// streaming: every survivor in a bin above the cutoff bin is written out in
-// one pass over the buffer, which also gathers the cutoff bin's entries; one
-// wave ranks those by (key descending, index ascending) and writes the first
-// `need`. A crowded or open-ended cutoff bin takes the radix select instead.
-__device__ void finish_survivors(Shared& sm, uint32_t n, uint32_t m, StreamBins bins, uint32_t hi,
-                                 int idx_bits, const Params& p, int64_t b, int32_t* orow) {
-    const Found f = find_rank_bin(sm, m);
-    const LdsSource src{&sm, n};
-    if (f.count > (uint32_t)kMaxCand || f.digit == (uint32_t)kBins - 1u) {
-        const Selection s = select_top(sm, src, m, n, bins.T, hi, idx_bits);
-        emit(sm, src, s, m, p, b, orow);
-        return;
-    }
-    const uint32_t d = f.digit;
-    const uint32_t need = m - f.above;
-    const bool whole = f.count == need;  // the cutoff bin is taken whole
-    src.for_each([&](uint32_t key, uint32_t idx) {
-        const uint32_t bk = bins(key);
-        out_append(sm, bk > d || (whole && bk == d), idx, m, p, b, orow);
-        const bool cand = !whole && bk == d;
-        const uint32_t slot = wave_reserve(&sm.ncand, cand);
-        if (cand && slot < (uint32_t)kMaxCand) {
-            sm.cand_key[slot] = key;
-            sm.cand_idx[slot] = idx;
-        }
-    });
-    if (whole) return;
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const uint32_t lane = lane_id();
-        const uint32_t nc = f.count;
-        const bool have = lane < nc;
-        const uint32_t kj = have ? sm.cand_key[lane] : 0u;
-        const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
-        uint32_t r = 0;  // candidates ranked before this one
-        for (uint32_t i = 0; i < nc; ++i) {
-            const uint32_t ki = sm.cand_key[i];
-            const uint32_t ii = sm.cand_idx[i];
-            r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
-        }
-        out_append(sm, have && r < need, ij, m, p, b, orow);
-    }
-}
-
-__device__ void load_row_to_lds(Shared& sm, const float* row, int64_t L) {
-    const f4* r4 = reinterpret_cast<const f4*>(row);
-    const int64_t nvec = L >> 2;
-    for (int64_t v = threadIdx.x; v < nvec; v += kThreads) {
-        const f4 x = r4[v];
-        const uint32_t i = (uint32_t)(4 * v);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            sm.key[i + c] = order_key(x[c]);
-            sm.idx[i + c] = i + (uint32_t)c;
-        }
-    }
-    for (int64_t i = 4 * nvec + threadIdx.x; i < L; i += kThreads) {
-        sm.key[i] = order_key(row[i]);
-        sm.idx[i] = (uint32_t)i;
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ int bits_for(int64_t L) {  // bits to hold indices 0..L-1, L >= 2
-    return 64 - __clzll((unsigned long long)(L - 1));
-}
-
-__global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
-    __shared__ Shared sm;
-    const int64_t b = blockIdx.x;
-    int64_t L = p.lengths ? (int64_t)p.lengths[b] : p.n_cols;
-    L = L < 0 ? 0 : (L > p.n_cols ? p.n_cols : L);
-    const int32_t k = p.k;
-    const uint32_t m = (uint32_t)(L < k ? L : k);
-    int32_t* orow = p.out + b * (int64_t)k;
-    const float* row = p.scores + b * p.row_stride;
-
-    for (int i = threadIdx.x; i < kBins; i += kThreads) sm.hist[i] = 0u;
-    if (threadIdx.x == 0) {
-        sm.count = 0u;
+    S::sync();
+    if (S::rank() == 0) {
+        sm.count[x] = 0u;
+        sm.vmax[x] = 0u;
         sm.emitted = 0u;
-        sm.vmax = 0u;
-        sm.smax = 0u;
         sm.ncand = 0u;
     }
-    for (int j = (int)m + threadIdx.x; j < k; j += kThreads) orow[j] = -1;
+    S::sync();
+}
+
+// ----------------------------------------------------------------------------
+// the kernel
+// ----------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
+    using B = BlockScope<kThreads>;
+    __shared__ Shared sm;
+    for (int i = threadIdx.x; i < 2 * kBins; i += kThreads) (&sm.hist[0][0])[i] = 0u;
+    for (int i = threadIdx.x; i < kBins; i += kThreads) sm.shist[i] = 0u;
+    if (threadIdx.x == 0) {
+        sm.count[0] = sm.count[1] = 0u;
+        sm.vmax[0] = sm.vmax[1] = 0u;
+        sm.emitted = sm.semitted = 0u;
+        sm.ncand = 0u;
+        sm.ndeferred = 0u;
+        sm.ndirect = 0u;
+        sm.n_claimed = sm.n_ready = sm.n_finished = 0u;
+        sm.last_row = -1;
+        sm.abort = 0u;
+        for (int s = 0; s < kSlots; ++s) {
+            sm.slot[s].valid = 0u;
+            sm.chunk_next[s] = 0u;
+            sm.left[s] = 0u;
+        }
+    }
+    __syncthreads();
+    build_queue(p, sm);
+    const uint32_t cap = (uint32_t)p.capacity;
+    const SelectLds sampler_lds{sm.shist, sm.sfound};
+
+    // start: the sampler wave claims rows 0 and 1; the streaming waves issue
+    // chunks of them while the whole workgroup finds row 0's cutoff
+    if (wave_id() == 1) {
+        claim_row(p, sm, sm.slot[0], sampler_lds, &sm.semitted);
+        claim_row(p, sm, sm.slot[1], sampler_lds, &sm.semitted);
+        if (lane_id() == 0) sm.n_claimed = 2u;
+    }
+    __syncthreads();
+    Chunk a, b;
+    Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0u, 0u, 0};
+    if (wave_id() >= kFirstStreamer) {
+        st.c = st.grab(st.i, 1, false);
+        if (st.c < kNone) st.load(a, st.i, st.c);
+    }
+    if (sm.slot[0].valid && sm.slot[0].kind == kKindSampled) sample_cutoff<B>(p, sm, sm.slot[0], sampler_lds);
+    if (threadIdx.x == 0) sm.n_ready = 1u;
     __syncthreads();
 
-    int code = TOPK_ROW_EMPTY;
-    uint32_t seen = (uint32_t)L;
-    if (m == 0) {
-        // idle row: only -1 slots
-    } else if (L <= k) {
-        for (int64_t i = threadIdx.x; i < L; i += kThreads) orow[i] = map_slot(p, b, (uint32_t)i);
-        code = TOPK_ROW_ALL;
-    } else {
-        const uint32_t cap = (uint32_t)p.capacity;
-        int path = p.force_path;
-        if (path == TOPK_PATH_AUTO) path = L <= (int64_t)cap ? TOPK_PATH_LDS : TOPK_PATH_SAMPLED;
-        code = TOPK_ROW_FULL_FORCED;
-        if (path == TOPK_PATH_LDS && L <= (int64_t)cap) {
-            load_row_to_lds(sm, row, L);
-            const LdsSource src{&sm, (uint32_t)L};
-            uint32_t lo, hi;
-            key_range(sm, src, lo, hi);
-            const Selection s = select_top(sm, src, m, (uint32_t)L, lo, hi, bits_for(L));
-            emit(sm, src, s, m, p, b, orow);
-            code = TOPK_ROW_LDS;
-        } else if (path == TOPK_PATH_SAMPLED) {
-            StreamBins bins;
-            uint32_t hi;
-            const uint32_t n = sampled_survivors(sm, row, L, m, cap, bins, hi);
-            seen = n;
-            if (n >= m && n <= cap) {
-                finish_survivors(sm, n, m, bins, hi, bits_for(L), p, b, orow);
-                code = TOPK_ROW_SAMPLED;
-            } else {
-                // the survivor histogram is of no use to the full-row passes
-                for (int i = threadIdx.x; i < kBins; i += kThreads) sm.hist[i] = 0u;
-                __syncthreads();
-                code = n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
+    if (wave_id() == 0) {
+        // finisher: rows in order; the last row is left to the whole workgroup
+        int last = -1;
+        for (int i = 0;; ++i) {
+            const int s = i % kSlots;
+            if (!wait_for(sm, &sm.n_claimed, (uint32_t)i + 1u) || !sm.slot[s].valid) break;
+            // row i's buffer is free: rows up to i - 1 are finished
+            append_tail(sm, sm.slot[s], i & 1, cap, load_tail(p, sm.slot[s]));
+            if (!wait_for(sm, &sm.n_claimed, (uint32_t)i + 2u)) break;
+            if (!sm.slot[(i + 1) % kSlots].valid) {
+                last = i;
+                break;
             }
+            if (!wait_for(sm, &sm.left[s], (uint32_t)kStreamers)) break;
+            finish_row<WaveScope>(p, sm, sm.slot[s], i & 1, cap);
+            if (lane_id() == 0) sm.left[s] = 0u;
+            publish(&sm.n_finished, (uint32_t)i + 1u);
         }
-        if (code >= TOPK_ROW_FULL_OVERFLOW) {
-            const RowSource src{row, L};
-            const Selection s = select_top(sm, src, m, (uint32_t)L, 0u, 0xFFFFFFFFu, bits_for(L));
-            emit(sm, src, s, m, p, b, orow);
+        if (lane_id() == 0) sm.last_row = last;
+    } else if (wave_id() == 1) {
+        // sampler: the cutoff of row j, then the claim of row j + 1, whose
+        // slot held row j - 3
+        for (int j = 1;; ++j) {
+            const int s = j % kSlots;
+            if (!sm.slot[s].valid) break;
+            if (sm.slot[s].kind == kKindSampled) sample_cutoff<WaveScope>(p, sm, sm.slot[s], sampler_lds);
+            publish(&sm.n_ready, (uint32_t)j + 1u);
+            if (j >= 3 && !wait_for(sm, &sm.n_finished, (uint32_t)j - 2u)) break;
+            const int sn = (j + 1) % kSlots;
+            if (lane_id() == 0) sm.chunk_next[sn] = 0u;
+            claim_row(p, sm, sm.slot[sn], sampler_lds, &sm.semitted);
+            publish(&sm.n_claimed, (uint32_t)j + 2u);
+        }
+    } else {
+        bool more = st.c != kEnd;
+        if (more && st.c == kNone) {
+            st.c = st.grab(st.i, INT32_MAX, false);
+            more = st.c != kEnd;
+            if (more) st.load(a, st.i, st.c);
+        }
+        while (more) {
+            more = st.step(a, b);
+            if (more) more = st.step(b, a);
         }
     }
-    if (p.row_stats != nullptr && threadIdx.x == 0) {
-        p.row_stats[2 * b + 0] = code;
-        p.row_stats[2 * b + 1] = (int32_t)seen;
+    __syncthreads();
+    if (sm.abort != 0u && threadIdx.x == 0) atomicAdd(&g_watchdog_trips, 1u);
+    if (sm.last_row >= 0 && sm.abort == 0u) {
+        const int r = sm.last_row;
+        finish_row<B>(p, sm, sm.slot[r % kSlots], r & 1, cap);
     }
+    __syncthreads();
+    const uint32_t nd = sm.ndeferred < (uint32_t)kMaxDeferred ? sm.ndeferred : (uint32_t)kMaxDeferred;
+    for (uint32_t j = 0; j < nd; ++j)
+        full_row<B>(p, SelectLds{sm.hist[0], sm.found}, &sm.emitted, sm.deferred[j], sm.deferred_code[j]);
+}
+
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 64) {
+        const int v = cached[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 }  // namespace
+}  // namespace topk
+
+using namespace topk;
 
 extern "C" {
 
@@ -698,6 +1055,13 @@ const char* topk_status_string(int status) {
 }
 
 int32_t topk_max_capacity(void) { return kCapacity; }
+
+uint32_t topk_watchdog_trips(void) {
+    unsigned int n = 0;
+    if (hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_watchdog_trips), sizeof(n), 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return 0xFFFFFFFFu;
+    return n;
+}
 
 int topk_select_ex(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
                    const int32_t* lengths, int32_t k, int32_t* out_idx,
@@ -719,13 +1083,15 @@ int topk_select_ex(const float* scores, int64_t batch, int64_t row_stride, int64
     if (scores == nullptr || out_idx == nullptr) return TOPK_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(scores) & 15u) != 0) return TOPK_ERR_ALIGN;
     if (batch > 1 && (row_stride & 3) != 0) return TOPK_ERR_ALIGN;
+    const int cus = device_cus();
+    if (cus <= 0) return TOPK_ERR_LAUNCH;
 
-    Params p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride,
-             page_size, k, opt.force_path, opt.capacity, opt.row_stats};
+    Params p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride, page_size, k,
+             opt.force_path, opt.capacity, opt.row_stats, batch};
     void* args[] = {&p};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_rows_kernel),
-                                         dim3((uint32_t)batch), dim3(kThreads), args, 0,
-                                         static_cast<hipStream_t>(hip_stream));
+    const int64_t grid = batch < cus ? batch : cus;
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_rows_kernel), dim3((uint32_t)grid),
+                                         dim3(kThreads), args, 0, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? TOPK_OK : TOPK_ERR_LAUNCH;
 }
 

@@ -17,7 +17,7 @@
  *    selected-value multiset is exact even when one coarse bin holds more
  *    candidates than any buffer; only equal scores may trade places.
  *  - vLLM PR #56346 report, implementation items 1-3: one launch serves long
- *    and short rows, lengths stay on the device, grid = one workgroup per row.
+ *    and short rows, and lengths stay on the device.
  *
  * Result, exactly: with L = clamp(lengths[b], 0, n_cols) and m = min(k, L),
  * slots [0, m) of out row b hold the m positions of [0, L) that rank first
@@ -27,17 +27,21 @@
  * every internal path, returns the same set.
  *
  * Memory: every pointer argument is a DEVICE pointer owned by the caller.
- * The library allocates, frees and retains nothing; it reads scores[b, 0:L),
+ * The library allocates, frees and retains nothing (one device word counts
+ * watchdog trips, see topk_watchdog_trips); it reads scores[b, 0:L),
  * lengths[0:batch) and the page-table entries of pages that hold a selected
- * position, and writes only out_idx[0:batch, 0:k).
+ * position, and writes only out_idx[0:batch, 0:k) (and row_stats).
  *
  * Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the default
- * stream) and never synchronise. Argument errors are returned synchronously
+ * stream) and never synchronise. Each call is one launch on that stream: a
+ * persistent kernel with one workgroup per compute unit, whose LDS (about
+ * 157 KB) leaves room for no other workgroup on the unit while it runs.
+ * Argument errors are returned synchronously
  * as a status code before anything is launched; device data (lengths, page
  * table contents) is never an error: lengths are clamped to [0, n_cols].
  * NaN inside [0, L) is outside the contract: the call stays memory-safe, but
- * which positions it selects is unspecified. The library keeps no global
- * state and is safe to call from several host threads.
+ * which positions it selects is unspecified. Calls are safe from several host
+ * threads.
  */
 #ifndef EXACT_TOPK_H
 #define EXACT_TOPK_H
@@ -60,15 +64,15 @@ extern "C" {
 
 /* internal paths (for topk_options.force_path and row statistics) */
 #define TOPK_PATH_AUTO 0
-#define TOPK_PATH_LDS 1      /* whole row held in LDS, exact select there (rows <= capacity) */
+#define TOPK_PATH_LDS 1      /* every position kept in LDS, exact select there (rows <= capacity) */
 #define TOPK_PATH_SAMPLED 2  /* sampled cutoff, one streaming pass, exact select on survivors */
 #define TOPK_PATH_FULLROW 3  /* full-row exact: histogram-only passes, one emission pass */
 
 /* row statistics codes, written to row_stats[2*b] */
 #define TOPK_ROW_EMPTY 0          /* m == 0: every slot -1 */
 #define TOPK_ROW_ALL 1            /* L <= k: every position selected */
-#define TOPK_ROW_LDS 2
-#define TOPK_ROW_SAMPLED 3
+#define TOPK_ROW_LDS 2            /* every position held in LDS */
+#define TOPK_ROW_SAMPLED 3        /* sampled cutoff, selected among the survivors */
 #define TOPK_ROW_FULL_OVERFLOW 4  /* sampled survivors exceeded the capacity */
 #define TOPK_ROW_FULL_UNDERFLOW 5 /* fewer sampled survivors than m */
 #define TOPK_ROW_FULL_FORCED 6    /* full-row path chosen by the caller, or LDS forced on a row above capacity */
@@ -107,7 +111,7 @@ int topk_select(const float* scores, int64_t batch, int64_t row_stride, int64_t 
  *  capacity    survivor capacity in entries, 1..topk_max_capacity() (0 = maximum);
  *              a small value makes the overflow fallback easy to reach
  *  row_stats   device int32 [batch, 2] or NULL: [2b] = TOPK_ROW_* code,
- *              [2b+1] = survivor count of the sampled pass (or L on other paths)
+ *              [2b+1] = survivors of the streaming pass (or L on the other paths)
  */
 typedef struct topk_options {
     int32_t force_path;
@@ -123,8 +127,17 @@ int topk_select_ex(const float* scores, int64_t batch, int64_t row_stride, int64
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* topk_status_string(int status);
 
-/* Largest survivor capacity (entries held in LDS per workgroup). */
+/* Largest survivor capacity (entries held in one LDS buffer). */
 int32_t topk_max_capacity(void);
+
+/*
+ * Workgroups that gave up a wait between their roles since the library was
+ * loaded, on the current device. Each wait is bounded (10 s) so that a defect
+ * ends the launch instead of hanging the GPU; a nonzero count means outputs
+ * of that launch are wrong. Synchronous (copies one word from the device);
+ * 0xFFFFFFFF if the copy fails.
+ */
+uint32_t topk_watchdog_trips(void);
 
 #ifdef __cplusplus
 }

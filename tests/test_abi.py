@@ -53,7 +53,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert header_functions() == sorted(
-        ["topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity"])
+        ["topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity",
+         "topk_watchdog_trips"])
 
 
 def test_every_declared_symbol_is_exported(lib):

@@ -61,6 +61,7 @@ def run(topk, wl, *, k=None, force=0, capacity=0, lengths=None, scores_dev=None,
     topk.topk_select_ex(s, ln, k, out, pt, wl.page_size, n_cols=n_cols or wl.n_cols,
                         force_path=force, capacity=capacity, row_stats=stats)
     torch.cuda.synchronize()
+    assert topk.topk_watchdog_trips() == 0, "a workgroup gave up waiting"
     h = buf.cpu().numpy()
     assert np.all(h[:GUARD] == CANARY) and np.all(h[GUARD + B * k:] == CANARY), "write outside out"
     return h[GUARD:GUARD + B * k].reshape(B, k), (stats.cpu().numpy() if want_stats else None)
@@ -268,3 +269,33 @@ def test_long_adversarial_rows(topk, width, k):
     for force in (0, 3):
         got, _ = run(topk, wl, force=force)
         assert_parity(wl, got, expect(wl))
+
+
+def test_plain_c_entry(topk):
+    # topk_select through the C ABI directly, three calls on one stream
+    wl = synth.mixed_rows(["normal", "onebin", "crowd4096", "signed_zero"], 50000, 777, seed=29)
+    s = to_dev(wl.scores)
+    ln = to_dev(wl.lengths)
+    out = torch.full((wl.batch, wl.k), CANARY, dtype=torch.int32, device="cuda")
+    lib = topk._load()
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        rc = lib.topk_select(s.data_ptr(), wl.batch, s.stride(0), wl.n_cols, ln.data_ptr(), wl.k,
+                             out.data_ptr(), None, 0, 0, stream)
+        assert rc == 0
+    torch.cuda.synchronize()
+    assert_parity(wl, out.cpu().numpy(), expect(wl))
+
+
+def test_deferred_list_overflow(topk):
+    # more rows forced to the full-row path than one workgroup can defer
+    rng = np.random.default_rng(30)
+    B, W, k = 256 * 80, 640, 9
+    scores = rng.standard_normal((B, W)).astype(np.float32)
+    lengths = rng.integers(k + 1, W + 1, B).astype(np.int32)
+    synth.poison_tails(scores, lengths)
+    wl = synth.Workload("many_fullrow", 30, scores, lengths, W, k)
+    got, stats = run(topk, wl, force=3, want_stats=True)
+    assert np.all(stats[:, 0] == 6)
+    bad = check_fast_raw(got, expect(wl), wl.lengths, wl.n_cols, wl.k)
+    assert not bad, bad[:10]

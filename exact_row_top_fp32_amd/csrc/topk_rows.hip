@@ -47,7 +47,11 @@ namespace {
 constexpr int kThreads = 1024;                            // 16 waves
 constexpr int kFirstStreamer = 2;                          // waves 2..15 stream
 constexpr int kCapacity = 7168;                            // survivor entries per buffer
-constexpr int kUnroll = 4;                                 // 16-byte loads per lane per chunk
+#ifndef TOPK_UNROLL
+#define TOPK_UNROLL 8
+#endif
+constexpr int kUnroll = TOPK_UNROLL;                       // 16-byte loads per lane per chunk
+constexpr int kPart = 4;                                   // loads filtered per LDS reservation
 constexpr int kChunkVec = 64 * kUnroll;                    // float4 groups per chunk
 constexpr int kRunLen = 64;                                // floats per contiguous sample run
 constexpr int kMaxRuns = 64;                               // runs per sample
@@ -145,8 +149,8 @@ __device__ __forceinline__ void put_stats(const Params& p, int64_t b, int code, 
     }
 }
 
-// Bin of a survivor in the histogram built while streaming: bins of width
-// 2^sh upward from the cutoff T, the last bin open-ended.
+// Bin of a survivor in the row's survivor histogram: bins of width 2^sh
+// upward from the cutoff T, the last bin open-ended.
 struct StreamBins {
     uint32_t T;
     uint32_t sh;
@@ -636,10 +640,7 @@ __device__ __forceinline__ void append_tail(Shared& sm, const RowSlot& R, int x,
         if (h && pos < cap) {
             sm.key[x][pos] = kk;
             sm.idx[x][pos] = (uint32_t)(R.L & ~(int64_t)3) + lane;
-            atomicAdd(&sm.hist[x][StreamBins{R.T, R.sh}(kk)], 1u);
         }
-        const uint32_t h_max = wave_max(h ? kk : 0u);
-        if (lane == 0) atomicMax(&sm.vmax[x], h_max);
     }
     WaveScope::sync();
 }
@@ -653,7 +654,7 @@ struct Streamer {
     uint32_t c;  // the chunk held
     int open;    // the row whose filter state below is loaded, or -1
     int ok;      // rows up to this one have their cutoff set and their buffer free
-    uint32_t T, sh, buf, hmax;
+    uint32_t T, buf;
     int64_t L;
 
     __device__ __forceinline__ void leave(int r) { publish_add(&sm.left[r % kSlots], 1u); }
@@ -684,30 +685,28 @@ struct Streamer {
         load_chunk(v, p.scores + R.b * p.row_stride, R.L, ch);
     }
 
-    // Appends the hits of chunk ch of row r (key >= T) to the row's buffer
-    // with one LDS atomic, and bins them; false once the row's count has
-    // passed the capacity. kNonNegT: T is the key of a non-negative float,
-    // so a signed compare of the raw bits decides.
-    template <bool kNonNegT>
-    __device__ __forceinline__ bool filter(const Chunk& x, uint32_t ch) {
+    // Appends the hits (key >= T) of loads [kPart H, kPart H + kPart) of
+    // chunk ch to the row's buffer with one LDS atomic; false
+    // once the row's count has passed the capacity. kNonNegT: T is the key of
+    // a non-negative float, so a signed compare of the raw bits decides.
+    template <bool kNonNegT, int H>
+    __device__ __forceinline__ bool filter_part(const Chunk& x, uint32_t ch) {
         const uint32_t lane = lane_id();
         const int64_t v0 = (int64_t)ch * kChunkVec + lane;
         const int32_t Ts = (int32_t)(T ^ 0x80000000u);
-        const StreamBins bins{T, sh};
         uint32_t* key = sm.key[buf];
         uint32_t* idx = sm.idx[buf];
-        uint32_t* hist = sm.hist[buf];
         auto hit = [&](float f) -> bool {
             if constexpr (kNonNegT) return (int32_t)__float_as_uint(f) >= Ts;
             else return order_key(f) >= T;
         };
         const int64_t nfull = L >> 2;
-        const f4 (&v)[kUnroll] = x.v;
-        uint64_t masks[4 * kUnroll];
+        const f4* v = x.v + kPart * H;
+        uint64_t masks[4 * kPart];
         uint32_t total = 0;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const bool ok = v0 + u * 64 < nfull;
+        for (int u = 0; u < kPart; ++u) {
+            const bool ok = v0 + (kPart * H + u) * 64 < nfull;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 masks[4 * u + e] = __ballot(ok && hit(v[u][e]));
@@ -721,25 +720,30 @@ struct Streamer {
         if (base >= cap) return false;
         uint32_t off = base;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t i0 = (uint32_t)(4 * (v0 + u * 64));
+        for (int u = 0; u < kPart; ++u) {
+            const uint32_t i0 = (uint32_t)(4 * (v0 + (kPart * H + u) * 64));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint64_t mk = masks[4 * u + e];
                 if ((mk >> lane) & 1u) {
                     const uint32_t pos = off + lanes_below(mk);
-                    const uint32_t kk = order_key(v[u][e]);
-                    hmax = max(hmax, kk);
                     if (pos < cap) {
-                        key[pos] = kk;
+                        key[pos] = order_key(v[u][e]);
                         idx[pos] = i0 + (uint32_t)e;
-                        atomicAdd(&hist[bins(kk)], 1u);
                     }
                 }
                 off += (uint32_t)__popcll(mk);
             }
         }
         return base + total <= cap;
+    }
+
+    template <bool kNonNegT, int H = 0>
+    __device__ __forceinline__ bool filter(const Chunk& x, uint32_t ch) {
+        static_assert(kUnroll % kPart == 0, "whole parts per chunk");
+        if (!filter_part<kNonNegT, H>(x, ch)) return false;
+        if constexpr (H + 1 < kUnroll / kPart) return filter<kNonNegT, H + 1>(x, ch);
+        return true;
     }
 
     __device__ __forceinline__ bool filter_held(const Chunk& v) {
@@ -751,7 +755,6 @@ struct Streamer {
             }
             const RowSlot& R = sm.slot[i % kSlots];
             T = R.T;
-            sh = R.sh;
             L = R.L;
             buf = (uint32_t)(i & 1);
             open = i;
@@ -761,9 +764,6 @@ struct Streamer {
 
     // Done with row r: its largest survivor key, then the count of waves out.
     __device__ __forceinline__ void close(int r) {
-        const uint32_t h = wave_max(hmax);
-        if (lane_id() == 0 && h != 0u) atomicMax(&sm.vmax[r & 1], h);
-        hmax = 0u;
         leave(r);
     }
 
@@ -798,12 +798,14 @@ struct Streamer {
 // ----------------------------------------------------------------------------
 
 // Scope S (wave 0 alone, or the whole workgroup for the last row): the exact
-// top m of row R from the n survivors in buffer x, using the histogram built
-// while streaming. Every survivor in a bin above the cutoff bin is written
-// out in one pass over the buffer, which also gathers the cutoff bin's
-// entries; one wave ranks those by (key descending, index ascending) and
-// writes the first `need`. A crowded or open-ended cutoff bin takes the radix
-// select over the buffer instead. Leaves buffer x's counters and histogram zero.
+// top m of row R from the n survivors in buffer x. One pass bins the
+// survivors upward from T and finds the largest; the bin holding the m-th
+// largest follows from the counts. Every survivor in a bin above it is
+// written out in a second pass over the buffer, which also gathers the
+// cutoff bin's entries; one wave ranks those by (key descending, index
+// ascending) and writes the first `need`. A crowded or open-ended cutoff bin
+// takes the radix select over the buffer instead. Leaves buffer x's counters
+// and histogram zero.
 template <class S>
 __device__ __forceinline__ void finish_row(const Params& p, Shared& sm, const RowSlot& R, int x, uint32_t cap) {
     constexpr bool kWave = S::kSize == 64;
@@ -812,12 +814,29 @@ __device__ __forceinline__ void finish_row(const Params& p, Shared& sm, const Ro
     uint32_t* hist = sm.hist[x];
     const SelectLds lds{hist, sm.found};
     if (n > cap || n < m) {
-        for (int i = S::rank(); i < kBins; i += S::kSize) hist[i] = 0u;
-        S::sync();
         const int code = n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
         if (S::first_wave()) defer_row(p, sm, lds, &sm.emitted, R.b, code);
     } else {
         const StreamBins bins{R.T, R.sh};
+        {
+            const uint32_t* K = sm.key[x];
+            uint32_t vm = 0u;
+            for (uint32_t e0 = S::rank(); e0 < n; e0 += 4 * S::kSize) {
+                uint32_t kk[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kk[j] = e0 + j * S::kSize < n ? K[e0 + j * S::kSize] : 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (e0 + j * S::kSize < n) {
+                        vm = max(vm, kk[j]);
+                        atomicAdd(&hist[bins(kk[j])], 1u);
+                    }
+                }
+            }
+            vm = wave_max(vm);
+            if (lane_id() == 0) atomicMax(&sm.vmax[x], vm);
+            S::sync();
+        }
         const Found f = find_rank_bin<S>(lds, m);
         if (f.count > (uint32_t)kMaxCand || f.digit == (uint32_t)kBins - 1u) {
             const LdsSource<S> src{sm.key[x], sm.idx[x], n};
@@ -956,7 +975,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     }
     __syncthreads();
     Chunk a, b;
-    Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0u, 0u, 0};
+    Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0};
     if (wave_id() >= kFirstStreamer) {
         st.c = st.grab(st.i, 1, false);
         if (st.c < kNone) st.load(a, st.i, st.c);

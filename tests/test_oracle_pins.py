@@ -67,6 +67,33 @@ def pin_brute_force(fn, seed=11, cases=300):
         assert chosen == min(tuple(sorted(s)) for s in valid), "ties must go to the lowest indices"
 
 
+def pin_pairwise_invariant(fn, seed=17, cases=40):
+    """Rows up to 512 from small alphabets: every selected value ranks at or
+    above every unselected one, no index repeats, exactly m are selected and
+    ties at the cutoff go to the lowest indices (O(L^2) pair checks)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(cases):
+        L = int(rng.integers(1, 513))
+        k = int(rng.integers(1, 600))
+        alpha = ALPHABET[rng.choice(len(ALPHABET), int(rng.integers(2, len(ALPHABET) + 1)), replace=False)]
+        row = np.full((1, L + 3), np.nan, np.float32)
+        row[0, :L] = rng.choice(alpha, L)
+        got = fn(row, np.array([L], np.int32), k, n_cols=L)[0]
+        m = min(k, L)
+        sel = got[:m]
+        assert np.all(got[m:] == -1) and len(set(sel.tolist())) == m
+        assert np.all((sel >= 0) & (sel < L))
+        keys = [rank_tuple(v) for v in row[0, :L]]
+        chosen = np.zeros(L, bool)
+        chosen[sel] = True
+        worst = min(keys[i] for i in sel)
+        for i in range(L):
+            if not chosen[i]:
+                assert keys[i] <= worst, "an unselected value ranks above a selected one"
+                if keys[i] == worst:
+                    assert all(j < i for j in sel if keys[j] == worst), "ties must go to the lowest indices"
+
+
 def pin_library_sort(fn, seed=12):
     """Sorted selected values equal numpy's and torch's sorts (no signed zeros)."""
     rng = np.random.default_rng(seed)
@@ -175,7 +202,7 @@ def pin_paged(fn):
         assert np.all(got[b, m:] == -1)
 
 
-ALL_PINS = [pin_brute_force, pin_library_sort, pin_closed_forms, pin_paged]
+ALL_PINS = [pin_brute_force, pin_pairwise_invariant, pin_library_sort, pin_closed_forms, pin_paged]
 
 
 # ----------------------------------------------------------------------------
@@ -258,7 +285,7 @@ MUTATIONS = ["ties_high_index", "no_signed_zero", "fp16_key", "drop_neginf",
 
 
 def test_python_statement_agrees_with_oracle():
-    for pin in (pin_brute_force, pin_closed_forms, pin_paged):
+    for pin in (pin_brute_force, pin_pairwise_invariant, pin_closed_forms, pin_paged):
         pin(py_oracle)
     wl = synth.c2(512, width=2048, rows_per_kind=1)
     assert np.array_equal(py_oracle(wl.scores, wl.lengths, wl.k), oracle.topk(wl.scores, wl.lengths, wl.k))

@@ -84,7 +84,14 @@ struct BlockScope {
     static constexpr int kSize = NT;
     __device__ static uint32_t rank() { return threadIdx.x; }
     __device__ static bool first_wave() { return threadIdx.x < 64; }
-    __device__ static void sync() { __syncthreads(); }
+    // A workgroup barrier that orders LDS only. Waves share data through LDS
+    // alone, so no wave has to wait for its outstanding global loads (a
+    // full __syncthreads would drain every wave's loads in flight).
+    __device__ static void sync() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
 };
 
 struct WaveScope {
@@ -170,14 +177,17 @@ __device__ __forceinline__ Found find_rank_bin(SelectLds lds, uint32_t rank) {
 // element sources: keys held in LDS, or a row of fp32 scores in global memory
 // ----------------------------------------------------------------------------
 
+// Survivors held in LDS as (raw score bits, position) pairs; yields keys.
 template <class S>
-struct LdsSource {
-    const uint32_t* key;
-    const uint32_t* idx;
+struct PairSource {
+    const uint2* entry;
     uint32_t n;
     template <class F>
     __device__ void for_each(F&& f) const {
-        for (uint32_t e = S::rank(); e < n; e += S::kSize) f(key[e], idx[e]);
+        for (uint32_t e = S::rank(); e < n; e += S::kSize) {
+            const uint2 v = entry[e];
+            f(order_key(__uint_as_float(v.x)), v.y);
+        }
     }
 };
 

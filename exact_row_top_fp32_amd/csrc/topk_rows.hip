@@ -12,14 +12,13 @@
 //    sampled cutoff, then exact selection among the survivors);
 //  * waves 2-15 read each row once, in chunks handed out one at a time, with
 //    16-byte buffer loads kept in flight across row boundaries, and append
-//    every key >= T to the row's buffer with one LDS atomic per wave and
-//    chunk, counting on past the capacity without writing, and binning
-//    survivors upward from T as they go (vLLM PR #56346 report,
-//    implementation item 1: ballot hit masks, in-wave prefix sums, one
-//    reservation per wave);
-//  * wave 0 finishes each row once every streaming wave has left it: every
-//    survivor above the cutoff bin is written out and the few in it are
-//    ranked exactly.
+//    every score with key >= T to the row's buffer with one LDS atomic per
+//    wave and 4 loads, counting on past the capacity without writing (vLLM
+//    PR #56346 report, implementation item 1: ballot hit masks, in-wave
+//    prefix sums, one reservation per wave);
+//  * wave 0 finishes each row once every streaming wave has left it: it
+//    bins the survivors upward from T, writes out every survivor above the
+//    bin holding the k-th largest and ranks the few in that bin exactly.
 //
 // Rows whose survivors overflow the buffer or fall short of k (and rows
 // forced to it) take the full-row path when the queue is done:
@@ -44,7 +43,10 @@
 namespace topk {
 namespace {
 
-constexpr int kThreads = 1024;                            // 16 waves
+#ifndef TOPK_WAVES
+#define TOPK_WAVES 12
+#endif
+constexpr int kThreads = 64 * TOPK_WAVES;                  // finisher, sampler, streamers
 constexpr int kFirstStreamer = 2;                          // waves 2..15 stream
 constexpr int kCapacity = 7168;                            // survivor entries per buffer
 #ifndef TOPK_UNROLL
@@ -95,8 +97,7 @@ struct RowSlot {
 };
 
 struct Shared {
-    uint32_t key[2][kCapacity];
-    uint32_t idx[2][kCapacity];
+    uint2 surv[2][kCapacity];   // survivors: (raw score bits, position)
     uint32_t hist[2][kBins];    // survivor histograms, all zero outside a row's use
     uint32_t skey[kMaxSample];  // the sampler's keys
     uint32_t shist[kBins];      // the sampler's histogram
@@ -117,8 +118,9 @@ struct Shared {
     uint32_t ncand;
     uint32_t smax;
     uint32_t slo;
-    uint32_t cand_key[kMaxCand];
-    uint32_t cand_idx[kMaxCand];
+    uint32_t cand_key[kMaxCand + 64];  // the last 64: a lane's write that is not kept
+    uint32_t cand_idx[kMaxCand + 64];
+    uint32_t sink[64];                 // a lane's output word that is not kept
     uint32_t ndeferred;
     int32_t deferred[kMaxDeferred];
     int32_t deferred_code[kMaxDeferred];
@@ -148,17 +150,6 @@ __device__ __forceinline__ void put_stats(const Params& p, int64_t b, int code, 
         p.row_stats[2 * b + 1] = (int32_t)seen;
     }
 }
-
-// Bin of a survivor in the row's survivor histogram: bins of width 2^sh
-// upward from the cutoff T, the last bin open-ended.
-struct StreamBins {
-    uint32_t T;
-    uint32_t sh;
-    __device__ __forceinline__ uint32_t operator()(uint32_t key) const {
-        const uint32_t d = (key - T) >> sh;
-        return d < (uint32_t)kBins ? d : (uint32_t)kBins - 1u;
-    }
-};
 
 // Position of this workgroup's j-th row in the queue: the order dealt out in
 // a snake (workgroup w takes w, 2G-1-w, 2G+w, ...), pairing long rows with
@@ -252,10 +243,11 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
         return;
     }
     const uint32_t n = (uint32_t)batch;
-    uint32_t* bucket = sm.key[0];  // per row: its length bucket, kBins for L <= k
-    int32_t* len = reinterpret_cast<int32_t*>(sm.idx[0]);
-    uint32_t* placed = sm.key[1];  // rows by bucket, any order within one
-    uint32_t* order = sm.idx[1];   // rows by bucket, index order within one
+    static_assert(2 * kCapacity >= 2 * kOrderMaxRows, "the queue fits the survivor buffers");
+    uint32_t* bucket = reinterpret_cast<uint32_t*>(sm.surv[0]);  // per row: its length bucket, kBins for L <= k
+    int32_t* len = reinterpret_cast<int32_t*>(bucket + kOrderMaxRows);
+    uint32_t* placed = reinterpret_cast<uint32_t*>(sm.surv[1]);  // rows by bucket, any order within one
+    uint32_t* order = placed + kOrderMaxRows;                       // rows by bucket, index order within one
     uint32_t* direct = sm.skey;    // this workgroup's rows with L <= k
     uint32_t* cnt = sm.hist[0];
     uint32_t* start = sm.hist[1];  // rows in higher buckets
@@ -392,7 +384,7 @@ __device__ __forceinline__ void claim_row(const Params& p, Shared& sm, RowSlot& 
     WaveScope::sync();
 }
 
-// Scope S: the cutoff of a sampled row. A sample of `runs` runs of 64
+// sample_cutoff, scope S: the cutoff of a sampled row. A sample of `runs` runs of 64
 // contiguous scores spread evenly over [0, L) gives T at or just below the
 // want-th largest sample key, want set so that the expected survivor count
 // sits several standard deviations above m (the number of sample keys above
@@ -406,42 +398,62 @@ __device__ __forceinline__ void claim_row(const Params& p, Shared& sm, RowSlot& 
 // bin is narrowed by further histograms until bins are at most 2^kFineShift
 // keys wide, and T is the lower edge of the last bin. The bin width of the
 // survivor histogram makes [T, sample max] cover about half its bins.
+// Where a row's sample lies: `runs` runs of kRunLen scores; run r starts at
+// floor(r (L - 64) / (runs - 1)) rounded down to a multiple of 4.
+struct SamplePlan {
+    int runs;
+    int nsv;  // 4-score groups in the sample
+    int64_t step_q;
+    uint32_t step_r;
+    __device__ __forceinline__ explicit SamplePlan(int64_t L) {
+        const int64_t fit = L / (2 * kRunLen);
+        runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
+        nsv = runs >= 2 ? runs * (kRunLen / 4) : 0;
+        const int64_t span = runs >= 2 ? (L - kRunLen) : 0;
+        step_q = runs >= 2 ? span / (runs - 1) : 0;
+        step_r = runs >= 2 ? (uint32_t)(span - step_q * (runs - 1)) : 0u;
+    }
+    // first score of 4-score group t of the sample
+    __device__ __forceinline__ int64_t group_start(int t) const {
+        const int r = t / (kRunLen / 4);
+        const int64_t start =
+            ((int64_t)r * step_q + (int64_t)(((uint32_t)r * step_r) / (uint32_t)(runs - 1))) & ~(int64_t)3;
+        return start + 4 * (t % (kRunLen / 4));
+    }
+};
+
+// Scope S: loads row R's sample from HBM straight into LDS, group t at
+// skey[4t, 4t + 4) whichever scope loads it (lane l of a wave writes 16
+// bytes at the wave's LDS base + 16 l), and waits for this wave's loads.
 template <class S>
-__device__ __forceinline__ void sample_cutoff(const Params& p, Shared& sm, RowSlot& R, SelectLds lds) {
+__device__ __forceinline__ void sample_load(const Params& p, Shared& sm, const RowSlot& R) {
     constexpr int kPer = (kMaxSample / 4 + S::kSize - 1) / S::kSize;  // 16-byte loads per lane
+    const SamplePlan plan(R.L);
+    const float* row = p.scores + R.b * p.row_stride;
+    const uint32_t wave_base = S::rank() & ~63u;
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+        const int t = h * S::kSize + (int)S::rank();
+        if (t < plan.nsv)
+            __builtin_amdgcn_global_load_lds(
+                row + plan.group_start(t),
+                (__attribute__((address_space(3))) void*)(sm.skey + 4 * (h * S::kSize + wave_base)), 16, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Scope S: the cutoff of row R from the sample in LDS (see sample_cutoff).
+template <class S>
+__device__ __forceinline__ void sample_select(Shared& sm, RowSlot& R, SelectLds lds) {
+    constexpr int kPer = (kMaxSample / 4 + S::kSize - 1) / S::kSize;  // groups per lane
     constexpr int kQ = 4;                                              // most keys kept per lane
     const int64_t L = R.L;
-    const float* row = p.scores + R.b * p.row_stride;
-    const int64_t fit = L / (2 * kRunLen);
-    const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
-    constexpr int kVecPerRun = kRunLen / 4;
-    const int nsv = runs >= 2 ? runs * kVecPerRun : 0;
-    // run r starts at floor(r * (L - 64) / (runs - 1)), rounded down to 4
-    const int64_t span_runs = runs >= 2 ? (L - kRunLen) : 0;
-    const int64_t step_q = runs >= 2 ? span_runs / (runs - 1) : 0;
-    const uint32_t step_r = runs >= 2 ? (uint32_t)(span_runs - step_q * (runs - 1)) : 0u;
+    const int nsv = SamplePlan(L).nsv;
     const uint32_t n = (uint32_t)nsv * 4;
     const float mu = (float)R.m * (float)n / (float)L;
     const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
     const uint32_t want = wantf < (float)n ? (uint32_t)wantf : 0u;  // 0: keep every key
     const uint32_t q = (want + S::kSize - 1) / S::kSize;
-    // lane l of a wave writes 16 bytes at the wave's LDS base + 16 l, so
-    // group t (4 scores) lands at skey[4t, 4t + 4)
-    const uint32_t wave_base = S::rank() & ~63u;
-#pragma unroll
-    for (int h = 0; h < kPer; ++h) {
-        const int t = h * S::kSize + (int)S::rank();
-        if (t < nsv) {
-            const int r = t / kVecPerRun;
-            const int64_t start =
-                ((int64_t)r * step_q + (int64_t)(((uint32_t)r * step_r) / (uint32_t)(runs - 1))) & ~(int64_t)3;
-            __builtin_amdgcn_global_load_lds(
-                row + start + 4 * (t % kVecPerRun),
-                (__attribute__((address_space(3))) void*)(sm.skey + 4 * (h * S::kSize + wave_base)), 16, 0, 0);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // each lane reads back only the groups its own loads wrote
     auto each_key = [&](auto&& f) {
 #pragma unroll 4
         for (int h = 0; h < kPer; ++h) {
@@ -515,6 +527,12 @@ __device__ __forceinline__ void sample_cutoff(const Params& p, Shared& sm, RowSl
         R.sh = (uint32_t)(wbits > kDigitBits - 1 ? wbits - (kDigitBits - 1) : 0);
     }
     S::sync();
+}
+
+template <class S>
+__device__ __forceinline__ void sample_cutoff(const Params& p, Shared& sm, RowSlot& R, SelectLds lds) {
+    sample_load<S>(p, sm, R);
+    sample_select<S>(sm, R, lds);
 }
 
 // ----------------------------------------------------------------------------
@@ -638,8 +656,7 @@ __device__ __forceinline__ void append_tail(Shared& sm, const RowSlot& R, int x,
         base = __builtin_amdgcn_readfirstlane(base);
         const uint32_t pos = base + lanes_below(mk);
         if (h && pos < cap) {
-            sm.key[x][pos] = kk;
-            sm.idx[x][pos] = (uint32_t)(R.L & ~(int64_t)3) + lane;
+            sm.surv[x][pos] = make_uint2(__float_as_uint(t), (uint32_t)(R.L & ~(int64_t)3) + lane);
         }
     }
     WaveScope::sync();
@@ -686,56 +703,65 @@ struct Streamer {
     }
 
     // Appends the hits (key >= T) of loads [kPart H, kPart H + kPart) of
-    // chunk ch to the row's buffer with one LDS atomic; false
-    // once the row's count has passed the capacity. kNonNegT: T is the key of
-    // a non-negative float, so a signed compare of the raw bits decides.
+    // chunk ch to the row's buffer with one LDS atomic; false once the row's
+    // count has passed the capacity. Survivors are stored as raw score bits
+    // with their positions; the finisher turns the bits into keys.
+    // kNonNegT: T is the key of a non-negative float, so a signed compare of
+    // the raw bits decides.
     template <bool kNonNegT, int H>
     __device__ __forceinline__ bool filter_part(const Chunk& x, uint32_t ch) {
-        const uint32_t lane = lane_id();
-        const int64_t v0 = (int64_t)ch * kChunkVec + lane;
+        const int64_t v0 = (int64_t)ch * kChunkVec + lane_id();
         const int32_t Ts = (int32_t)(T ^ 0x80000000u);
-        uint32_t* key = sm.key[buf];
-        uint32_t* idx = sm.idx[buf];
+        const int64_t nfull = L >> 2;
         auto hit = [&](float f) -> bool {
             if constexpr (kNonNegT) return (int32_t)__float_as_uint(f) >= Ts;
             else return order_key(f) >= T;
         };
-        const int64_t nfull = L >> 2;
-        const f4* v = x.v + kPart * H;
-        uint64_t masks[4 * kPart];
+        // lanes whose group of load u lies inside the row (all but the
+        // row's last chunk: every lane)
+        uint64_t okm[kPart];
+        uint64_t mk[4 * kPart];
         uint32_t total = 0;
 #pragma unroll
         for (int u = 0; u < kPart; ++u) {
-            const bool ok = v0 + (kPart * H + u) * 64 < nfull;
+            okm[u] = __ballot(v0 + (kPart * H + u) * 64 < nfull);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                masks[4 * u + e] = __ballot(ok && hit(v[u][e]));
-                total += (uint32_t)__popcll(masks[4 * u + e]);
+                mk[4 * u + e] = __ballot(hit(x.v[kPart * H + u][e])) & okm[u];
+                total += (uint32_t)__popcll(mk[4 * u + e]);
             }
         }
         if (total == 0) return true;
         uint32_t base = 0u;
-        if (lane == 0) base = atomicAdd(&sm.count[buf], total);
+        if (lane_id() == 0) base = atomicAdd(&sm.count[buf], total);
         base = __builtin_amdgcn_readfirstlane(base);
         if (base >= cap) return false;
-        uint32_t off = base;
+        uint2* sv = sm.surv[buf];
+        auto append = [&](auto check) {
+            uint32_t off = base;
 #pragma unroll
-        for (int u = 0; u < kPart; ++u) {
-            const uint32_t i0 = (uint32_t)(4 * (v0 + (kPart * H + u) * 64));
+            for (int u = 0; u < kPart; ++u) {
+                const uint32_t i0 = (uint32_t)(4 * (v0 + (kPart * H + u) * 64));
+                const bool ok = v0 + (kPart * H + u) * 64 < nfull;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint64_t mk = masks[4 * u + e];
-                if ((mk >> lane) & 1u) {
-                    const uint32_t pos = off + lanes_below(mk);
-                    if (pos < cap) {
-                        key[pos] = order_key(v[u][e]);
-                        idx[pos] = i0 + (uint32_t)e;
+                for (int e = 0; e < 4; ++e) {
+                    const float f = x.v[kPart * H + u][e];
+                    // the compare again, rather than a kept flag, so that
+                    // its lane mask drives the append directly
+                    if (ok && hit(f)) {
+                        const uint64_t m = mk[4 * u + e];
+                        const uint32_t pos =
+                            __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, off));
+                        if (check(pos)) sv[pos] = make_uint2(__float_as_uint(f), i0 + (uint32_t)e);
                     }
+                    off += (uint32_t)__popcll(mk[4 * u + e]);
                 }
-                off += (uint32_t)__popcll(mk);
             }
-        }
-        return base + total <= cap;
+        };
+        const bool fits = base + total <= cap;
+        if (fits) append([](uint32_t) { return true; });
+        else append([&](uint32_t pos) { return pos < cap; });
+        return fits;
     }
 
     template <bool kNonNegT, int H = 0>
@@ -798,132 +824,177 @@ struct Streamer {
 // ----------------------------------------------------------------------------
 
 // Scope S (wave 0 alone, or the whole workgroup for the last row): the exact
-// top m of row R from the n survivors in buffer x. One pass bins the
-// survivors upward from T and finds the largest; the bin holding the m-th
-// largest follows from the counts. Every survivor in a bin above it is
-// written out in a second pass over the buffer, which also gathers the
-// cutoff bin's entries; one wave ranks those by (key descending, index
-// ascending) and writes the first `need`. A crowded or open-ended cutoff bin
-// takes the radix select over the buffer instead. Leaves buffer x's counters
-// and histogram zero.
+// top m of row R from its n survivors in buffer x, k <= m <= n <= capacity.
+// One pass bins the survivors upward from T and finds the largest; the bin
+// holding the m-th largest follows from the counts. Every survivor in a bin
+// above it is written out in a second pass over the buffer, which also
+// gathers the cutoff bin's entries; one wave ranks those by (key descending,
+// index ascending) and writes the first `need`. A crowded or open-ended
+// cutoff bin takes the radix select over the buffer instead.
+// kNonNegT: T is the key of a non-negative float, so every survivor is one
+// too and its raw bits order like its key (key = bits + 2^31); the passes
+// then compare raw bits with thresholds moved into that space.
+template <class S, bool kNonNegT>
+__device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, const RowSlot& R, int x, uint32_t n,
+                                               SelectLds lds) {
+    constexpr bool kWave = S::kSize == 64;
+    const uint32_t m = R.m;
+    uint32_t* hist = lds.hist;
+    const uint2* E = sm.surv[x];
+    // the value survivors are compared in: raw bits, or the key
+    auto val = [](uint32_t bits) -> uint32_t {
+        if constexpr (kNonNegT) return bits;
+        else return order_key(__uint_as_float(bits));
+    };
+    constexpr uint32_t kShift = kNonNegT ? 0x80000000u : 0u;  // key = val + kShift
+    const uint32_t Tv = R.T - kShift;
+    const uint32_t sh = R.sh;
+    // one wave reads kU entries per lane per step, all loads issued before
+    // any is used; reads past n stay inside the buffer (its capacity is a
+    // multiple of kU * 64) and are ignored
+    constexpr int kU = kWave ? 8 : 1;
+    static_assert(!kWave || kCapacity % (kU * 64) == 0, "unmasked reads stay in the buffer");
+    {
+        // bin the survivors and find the largest
+        uint32_t vm = 0u;
+        for (uint32_t e0 = kWave ? 0u : S::rank(); e0 < n; e0 += kU * S::kSize) {
+            uint2 v[kU];
+#pragma unroll
+            for (int j = 0; j < kU; ++j) v[j] = E[e0 + j * S::kSize + (kWave ? lane_id() : 0u)];
+#pragma unroll
+            for (int j = 0; j < kU; ++j) {
+                // no branch per entry: an entry past n adds zero
+                const bool ok = e0 + j * S::kSize + (kWave ? lane_id() : 0u) < n;
+                const uint32_t kv = val(v[j].x);
+                vm = max(vm, ok ? kv : 0u);
+                const uint32_t d = (kv - Tv) >> sh;
+                atomicAdd(&hist[d < (uint32_t)kBins ? d : (uint32_t)kBins - 1u], ok ? 1u : 0u);
+            }
+        }
+        vm = wave_max(vm);
+        if (lane_id() == 0) atomicMax(&sm.vmax[x], vm + kShift);
+        S::sync();
+    }
+    const Found f = find_rank_bin<S>(lds, m);
+    if (f.count > (uint32_t)kMaxCand || f.digit == (uint32_t)kBins - 1u) {
+        const PairSource<S> src{E, n};
+        const Selection s = select_top<S>(lds, src, m, n, R.T, sm.vmax[x], bits_for(R.L));
+        OutRow out = out_row(p, R.b, m, &sm.emitted);
+        emit(src, s, out);
+        return;
+    }
+    const uint32_t need = m - f.above;
+    const bool whole = f.count == need;  // the cutoff bin is taken whole
+    // bin f.digit is [lo, hi) in key space, hi <= 2^32; in val space:
+    // above <=> val > t_above, in the bin <=> !above && val >= t_lo
+    const uint64_t hi = (uint64_t)R.T + ((uint64_t)(f.digit + 1u) << sh);
+    const uint32_t t_above = (hi > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)(hi - 1u)) - kShift;
+    const uint32_t t_lo = R.T + (f.digit << sh) - kShift;  // the bin holds a survivor, so no overflow
+    if constexpr (kWave) {
+        // Selected positions are compacted in place into the buffer's first
+        // words (after a step's entries are read, the selected count cannot
+        // pass the words already read), then copied to the output row with
+        // coalesced stores. Within a step each lane marks its taken entries
+        // and cutoff-bin candidates in bit masks; one wave prefix sum of the
+        // packed counts places them.
+        const uint32_t lane = lane_id();
+        uint32_t* stage = reinterpret_cast<uint32_t*>(sm.surv[x]);
+        uint32_t next = 0u, ncand = 0u;
+        for (uint32_t e0 = 0; e0 < n; e0 += kU * 64) {
+            uint2 v[kU];
+#pragma unroll
+            for (int j = 0; j < kU; ++j) v[j] = E[e0 + 64 * j + lane];
+            uint32_t tmask = 0u, cmask = 0u;
+#pragma unroll
+            for (int j = 0; j < kU; ++j) {
+                const bool ok = e0 + 64 * j + lane < n;
+                const uint32_t kv = val(v[j].x);
+                tmask |= (ok && (whole ? kv >= t_lo : kv > t_above)) ? 1u << j : 0u;
+                cmask |= (ok && !whole && kv >= t_lo && kv <= t_above) ? 1u << j : 0u;
+            }
+            const uint32_t packed = (uint32_t)__popc(tmask) | ((uint32_t)__popc(cmask) << 16);
+            const uint32_t incl = wave_inclusive_sum(packed);
+            const uint32_t excl = incl - packed;
+            uint32_t ts = next + (excl & 0xFFFFu);
+            uint32_t cs = ncand + (excl >> 16);
+            const uint32_t total = __shfl(incl, 63, 64);
+            next += total & 0xFFFFu;
+            ncand += total >> 16;
+            // no branch per entry: a lane's write that is not kept goes to
+            // a word of its own
+#pragma unroll
+            for (int j = 0; j < kU; ++j) {
+                const uint32_t tb = (tmask >> j) & 1u;
+                *(tb ? stage + ts : sm.sink + lane) = v[j].y;
+                ts += tb;
+                const uint32_t cb = (cmask >> j) & 1u;
+                const uint32_t c_at = cb && cs < (uint32_t)kMaxCand ? cs : (uint32_t)kMaxCand + lane;
+                sm.cand_key[c_at] = val(v[j].x);
+                sm.cand_idx[c_at] = v[j].y;
+                cs += cb;
+            }
+        }
+        if (!whole) {
+            S::sync();
+            const uint32_t nc = f.count;
+            const bool have = lane < nc;
+            const uint32_t kj = have ? sm.cand_key[lane] : 0u;
+            const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
+            uint32_t r = 0;  // candidates ranked before this one
+            for (uint32_t i = 0; i < nc; ++i) {
+                const uint32_t ki = sm.cand_key[i];
+                const uint32_t ii = sm.cand_idx[i];
+                r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
+            }
+            if (have && r < need) stage[next + r] = ij;
+        }
+        S::sync();
+        const OutRow out = out_row(p, R.b, m, nullptr);
+        for (uint32_t i = lane; i < m; i += 64) out.row[i] = out.map(stage[i]);
+    } else {
+        OutRow out = out_row(p, R.b, m, &sm.emitted);
+        for (uint32_t e = S::rank(); e < n; e += S::kSize) {
+            const uint2 v = E[e];
+            const uint32_t kv = val(v.x);
+            out.append(whole ? kv >= t_lo : kv > t_above, v.y);
+            const bool cand = !whole && kv >= t_lo && kv <= t_above;
+            const uint32_t slot = wave_reserve(&sm.ncand, cand);
+            if (cand && slot < (uint32_t)kMaxCand) {
+                sm.cand_key[slot] = kv;
+                sm.cand_idx[slot] = v.y;
+            }
+        }
+        S::sync();
+        if (!whole && S::first_wave()) {
+            const uint32_t lane = lane_id();
+            const uint32_t nc = f.count;
+            const bool have = lane < nc;
+            const uint32_t kj = have ? sm.cand_key[lane] : 0u;
+            const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
+            uint32_t r = 0;
+            for (uint32_t i = 0; i < nc; ++i) {
+                const uint32_t ki = sm.cand_key[i];
+                const uint32_t ii = sm.cand_idx[i];
+                r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
+            }
+            out.append(have && r < need, ij);
+        }
+    }
+}
+
+// Scope S: finishes row R from buffer x, or defers it to the full-row path
+// when its survivors overflowed the buffer or fell short of m. Leaves buffer
+// x's counters and histogram zero.
 template <class S>
 __device__ __forceinline__ void finish_row(const Params& p, Shared& sm, const RowSlot& R, int x, uint32_t cap) {
-    constexpr bool kWave = S::kSize == 64;
     const uint32_t n = sm.count[x];
-    const uint32_t m = R.m;
-    uint32_t* hist = sm.hist[x];
-    const SelectLds lds{hist, sm.found};
-    if (n > cap || n < m) {
+    const SelectLds lds{sm.hist[x], sm.found};
+    if (n > cap || n < R.m) {
         const int code = n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
         if (S::first_wave()) defer_row(p, sm, lds, &sm.emitted, R.b, code);
     } else {
-        const StreamBins bins{R.T, R.sh};
-        {
-            const uint32_t* K = sm.key[x];
-            uint32_t vm = 0u;
-            for (uint32_t e0 = S::rank(); e0 < n; e0 += 4 * S::kSize) {
-                uint32_t kk[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kk[j] = e0 + j * S::kSize < n ? K[e0 + j * S::kSize] : 0u;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (e0 + j * S::kSize < n) {
-                        vm = max(vm, kk[j]);
-                        atomicAdd(&hist[bins(kk[j])], 1u);
-                    }
-                }
-            }
-            vm = wave_max(vm);
-            if (lane_id() == 0) atomicMax(&sm.vmax[x], vm);
-            S::sync();
-        }
-        const Found f = find_rank_bin<S>(lds, m);
-        if (f.count > (uint32_t)kMaxCand || f.digit == (uint32_t)kBins - 1u) {
-            const LdsSource<S> src{sm.key[x], sm.idx[x], n};
-            const Selection s = select_top<S>(lds, src, m, n, R.T, sm.vmax[x], bits_for(R.L));
-            OutRow out = out_row(p, R.b, m, &sm.emitted);
-            emit(src, s, out);
-        } else {
-            const uint32_t d = f.digit;
-            const uint32_t need = m - f.above;
-            const bool whole = f.count == need;  // the cutoff bin is taken whole
-            const uint32_t* K = sm.key[x];
-            const uint32_t* I = sm.idx[x];
-            if constexpr (kWave) {
-                // every lane runs every iteration, so per-lane slot counters
-                // stay in step across the wave
-                const uint32_t lane = lane_id();
-                WaveOutRow out{out_row(p, R.b, m, nullptr), 0u};
-                uint32_t ncand = 0u;
-                for (uint32_t e0 = 0; e0 < n; e0 += 4 * 64) {
-                    uint32_t kk[4], ii[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t e = e0 + 64 * j + lane;
-                        kk[j] = e < n ? K[e] : 0u;
-                        ii[j] = e < n ? I[e] : 0u;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const bool ok = e0 + 64 * j + lane < n;
-                        const uint32_t bk = bins(kk[j]);
-                        out.append(ok && (bk > d || (whole && bk == d)), ii[j]);
-                        const bool cand = ok && !whole && bk == d;
-                        const uint64_t cm = __ballot(cand);
-                        if (cand) {
-                            const uint32_t slot = ncand + lanes_below(cm);
-                            if (slot < (uint32_t)kMaxCand) {
-                                sm.cand_key[slot] = kk[j];
-                                sm.cand_idx[slot] = ii[j];
-                            }
-                        }
-                        ncand += (uint32_t)__popcll(cm);
-                    }
-                }
-                if (!whole) {
-                    S::sync();
-                    const uint32_t nc = f.count;
-                    const bool have = lane < nc;
-                    const uint32_t kj = have ? sm.cand_key[lane] : 0u;
-                    const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
-                    uint32_t r = 0;  // candidates ranked before this one
-                    for (uint32_t i = 0; i < nc; ++i) {
-                        const uint32_t ki = sm.cand_key[i];
-                        const uint32_t ii = sm.cand_idx[i];
-                        r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
-                    }
-                    out.append(have && r < need, ij);
-                }
-            } else {
-                OutRow out = out_row(p, R.b, m, &sm.emitted);
-                for (uint32_t e = S::rank(); e < n; e += S::kSize) {
-                    const uint32_t kk = K[e], ii = I[e];
-                    const uint32_t bk = bins(kk);
-                    out.append(bk > d || (whole && bk == d), ii);
-                    const bool cand = !whole && bk == d;
-                    const uint32_t slot = wave_reserve(&sm.ncand, cand);
-                    if (cand && slot < (uint32_t)kMaxCand) {
-                        sm.cand_key[slot] = kk;
-                        sm.cand_idx[slot] = ii;
-                    }
-                }
-                S::sync();
-                if (!whole && S::first_wave()) {
-                    const uint32_t lane = lane_id();
-                    const uint32_t nc = f.count;
-                    const bool have = lane < nc;
-                    const uint32_t kj = have ? sm.cand_key[lane] : 0u;
-                    const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
-                    uint32_t r = 0;
-                    for (uint32_t i = 0; i < nc; ++i) {
-                        const uint32_t ki = sm.cand_key[i];
-                        const uint32_t ii = sm.cand_idx[i];
-                        r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
-                    }
-                    out.append(have && r < need, ij);
-                }
-            }
-        }
+        if (R.T >= 0x80000000u) finish_sampled<S, true>(p, sm, R, x, n, lds);
+        else finish_sampled<S, false>(p, sm, R, x, n, lds);
         if (S::rank() == 0) put_stats(p, R.b, R.kind == kKindAll ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED, n);
     }
     S::sync();
@@ -961,28 +1032,30 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
             sm.left[s] = 0u;
         }
     }
-    __syncthreads();
+    B::sync();
     build_queue(p, sm);
     const uint32_t cap = (uint32_t)p.capacity;
     const SelectLds sampler_lds{sm.shist, sm.sfound};
 
-    // start: the sampler wave claims rows 0 and 1; the streaming waves issue
-    // chunks of them while the whole workgroup finds row 0's cutoff
+    // start: the sampler wave claims rows 0 and 1, and the whole workgroup
+    // finds row 0's cutoff (every wave loads a share of the sample) before
+    // any streaming load is issued: queued streaming loads would hold the
+    // sample's loads, and the waves issuing them, back
     if (wave_id() == 1) {
         claim_row(p, sm, sm.slot[0], sampler_lds, &sm.semitted);
         claim_row(p, sm, sm.slot[1], sampler_lds, &sm.semitted);
         if (lane_id() == 0) sm.n_claimed = 2u;
     }
-    __syncthreads();
+    B::sync();
+    if (sm.slot[0].valid && sm.slot[0].kind == kKindSampled) {
+        sample_load<B>(p, sm, sm.slot[0]);
+        B::sync();
+        sample_select<B>(sm, sm.slot[0], sampler_lds);
+    }
+    if (threadIdx.x == 0) sm.n_ready = 1u;
+    B::sync();
     Chunk a, b;
     Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0};
-    if (wave_id() >= kFirstStreamer) {
-        st.c = st.grab(st.i, 1, false);
-        if (st.c < kNone) st.load(a, st.i, st.c);
-    }
-    if (sm.slot[0].valid && sm.slot[0].kind == kKindSampled) sample_cutoff<B>(p, sm, sm.slot[0], sampler_lds);
-    if (threadIdx.x == 0) sm.n_ready = 1u;
-    __syncthreads();
 
     if (wave_id() == 0) {
         // finisher: rows in order; the last row is left to the whole workgroup
@@ -990,8 +1063,11 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         for (int i = 0;; ++i) {
             const int s = i % kSlots;
             if (!wait_for(sm, &sm.n_claimed, (uint32_t)i + 1u) || !sm.slot[s].valid) break;
-            // row i's buffer is free: rows up to i - 1 are finished
-            append_tail(sm, sm.slot[s], i & 1, cap, load_tail(p, sm.slot[s]));
+            // row i's buffer is free (rows up to i - 1 are finished); its
+            // tail is filtered once its cutoff is set
+            const float tail = load_tail(p, sm.slot[s]);
+            if (!wait_for(sm, &sm.n_ready, (uint32_t)i + 1u)) break;
+            append_tail(sm, sm.slot[s], i & 1, cap, tail);
             if (!wait_for(sm, &sm.n_claimed, (uint32_t)i + 2u)) break;
             if (!sm.slot[(i + 1) % kSlots].valid) {
                 last = i;
@@ -1018,24 +1094,21 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
             publish(&sm.n_claimed, (uint32_t)j + 2u);
         }
     } else {
+        st.c = st.grab(st.i, INT32_MAX, false);
+        st.load(a, st.i, st.c);
         bool more = st.c != kEnd;
-        if (more && st.c == kNone) {
-            st.c = st.grab(st.i, INT32_MAX, false);
-            more = st.c != kEnd;
-            if (more) st.load(a, st.i, st.c);
-        }
         while (more) {
             more = st.step(a, b);
             if (more) more = st.step(b, a);
         }
     }
-    __syncthreads();
+    B::sync();
     if (sm.abort != 0u && threadIdx.x == 0) atomicAdd(&g_watchdog_trips, 1u);
     if (sm.last_row >= 0 && sm.abort == 0u) {
         const int r = sm.last_row;
         finish_row<B>(p, sm, sm.slot[r % kSlots], r & 1, cap);
     }
-    __syncthreads();
+    B::sync();
     const uint32_t nd = sm.ndeferred < (uint32_t)kMaxDeferred ? sm.ndeferred : (uint32_t)kMaxDeferred;
     for (uint32_t j = 0; j < nd; ++j)
         full_row<B>(p, SelectLds{sm.hist[0], sm.found}, &sm.emitted, sm.deferred[j], sm.deferred_code[j]);

@@ -149,12 +149,15 @@ def main() -> int:
     warm_us = {n: np.array([a.elapsed_time(b) * 1e3 for a, b in ev[n]]) for n in names}
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
 
-    # cold: overwrite 1 GiB between launches so neither L2 nor MALL holds the rows
+    # cold: write then read 1 GiB between launches, so that neither L2 nor
+    # MALL holds the rows, and no dirty lines of the write are still waiting
+    # to be written back when the timed launch starts
     scratch = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
     cold_us = {n: [] for n in names}
     for i in range(args.cold_iters):
         for n in names:
             scratch.fill_(float(i))
+            scratch.sum()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             launch(n)

@@ -38,26 +38,46 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Cross-lane steps use DPP row operations (VALU only; no LDS round trip).
+// dpp controls: row_shr:n = 0x110 + n, row_bcast:15 = 0x142 (lane 15 of a
+// row to the next row), row_bcast:31 = 0x143 (lane 31 to rows 2 and 3). A
+// lane whose source lies outside its row, or whose row is masked off, takes
+// `fill`. Every lane of the wave must be active.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t fill, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)x, kCtrl, kRowMask, 0xF, false);
+}
+
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(x, d, 64);
-        if (lane >= (uint32_t)d) x += y;
-    }
+    x += dpp<0x111>(0u, x);  // within rows of 16: Hillis-Steele over 1, 2, 4, 8
+    x += dpp<0x112>(0u, x);
+    x += dpp<0x114>(0u, x);
+    x += dpp<0x118>(0u, x);
+    x += dpp<0x142, 0xA>(0u, x);  // rows 1 and 3 add the row before
+    x += dpp<0x143, 0xC>(0u, x);  // rows 2 and 3 add rows 0 and 1
     return x;
 }
 
+// Reductions: each row's lane 15 ends up holding its row's result; the four
+// are combined in scalar registers, so the result is wave-uniform.
 __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x = max(x, (uint32_t)__shfl_xor(x, d, 64));
-    return x;
+    x = max(x, dpp<0x111>(0u, x));
+    x = max(x, dpp<0x112>(0u, x));
+    x = max(x, dpp<0x114>(0u, x));
+    x = max(x, dpp<0x118>(0u, x));
+    const uint32_t a = __builtin_amdgcn_readlane(x, 15), b = __builtin_amdgcn_readlane(x, 31);
+    const uint32_t c = __builtin_amdgcn_readlane(x, 47), d = __builtin_amdgcn_readlane(x, 63);
+    return max(max(a, b), max(c, d));
 }
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x = min(x, (uint32_t)__shfl_xor(x, d, 64));
-    return x;
+    x = min(x, dpp<0x111>(0xFFFFFFFFu, x));
+    x = min(x, dpp<0x112>(0xFFFFFFFFu, x));
+    x = min(x, dpp<0x114>(0xFFFFFFFFu, x));
+    x = min(x, dpp<0x118>(0xFFFFFFFFu, x));
+    const uint32_t a = __builtin_amdgcn_readlane(x, 15), b = __builtin_amdgcn_readlane(x, 31);
+    const uint32_t c = __builtin_amdgcn_readlane(x, 47), d = __builtin_amdgcn_readlane(x, 63);
+    return min(min(a, b), min(c, d));
 }
 
 // Slot for every active lane with `pred` from a shared LDS counter: one
@@ -68,7 +88,7 @@ __device__ __forceinline__ uint32_t wave_reserve(uint32_t* counter, bool pred) {
     if (mask != 0) {
         const int leader = __ffsll((unsigned long long)mask) - 1;
         if ((int)lane_id() == leader) base = atomicAdd(counter, (uint32_t)__popcll(mask));
-        base = __shfl(base, leader, 64);
+        base = __builtin_amdgcn_readlane(base, leader);
     }
     return base + lanes_below(mask);
 }

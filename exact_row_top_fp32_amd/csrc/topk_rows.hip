@@ -271,7 +271,7 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
         uint32_t own = 0;
         for (int j = 0; j < 32; ++j) own += c[j];
         const uint32_t incl = wave_inclusive_sum(own);
-        const uint32_t total = __shfl(incl, 63, 64);
+        const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
         uint32_t above = total - incl;  // rows in the buckets of higher lanes
         for (int j = 31; j >= 0; --j) {
             start[32 * lane + j] = above;
@@ -823,6 +823,19 @@ struct Streamer {
 // finishing a row from its survivors
 // ----------------------------------------------------------------------------
 
+// One wave: lane l < nc holds candidate (key kj, index ij); returns how many
+// of the nc candidates rank before it (key descending, index ascending).
+// Candidates are read from the other lanes' registers, not from LDS.
+__device__ __forceinline__ uint32_t rank_in_wave(uint32_t kj, uint32_t ij, uint32_t nc) {
+    uint32_t r = 0;
+    for (uint32_t i = 0; i < nc; ++i) {
+        const uint32_t ki = __builtin_amdgcn_readlane(kj, i);
+        const uint32_t ii = __builtin_amdgcn_readlane(ij, i);
+        r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
+    }
+    return r;
+}
+
 // Scope S (wave 0 alone, or the whole workgroup for the last row): the exact
 // top m of row R from its n survivors in buffer x, k <= m <= n <= capacity.
 // One pass bins the survivors upward from T and finds the largest; the bin
@@ -917,7 +930,7 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
             const uint32_t excl = incl - packed;
             uint32_t ts = next + (excl & 0xFFFFu);
             uint32_t cs = ncand + (excl >> 16);
-            const uint32_t total = __shfl(incl, 63, 64);
+            const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
             next += total & 0xFFFFu;
             ncand += total >> 16;
             // no branch per entry: a lane's write that is not kept goes to
@@ -940,12 +953,7 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
             const bool have = lane < nc;
             const uint32_t kj = have ? sm.cand_key[lane] : 0u;
             const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
-            uint32_t r = 0;  // candidates ranked before this one
-            for (uint32_t i = 0; i < nc; ++i) {
-                const uint32_t ki = sm.cand_key[i];
-                const uint32_t ii = sm.cand_idx[i];
-                r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
-            }
+            const uint32_t r = rank_in_wave(kj, ij, nc);
             if (have && r < need) stage[next + r] = ij;
         }
         S::sync();
@@ -971,12 +979,7 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
             const bool have = lane < nc;
             const uint32_t kj = have ? sm.cand_key[lane] : 0u;
             const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
-            uint32_t r = 0;
-            for (uint32_t i = 0; i < nc; ++i) {
-                const uint32_t ki = sm.cand_key[i];
-                const uint32_t ii = sm.cand_idx[i];
-                r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
-            }
+            const uint32_t r = rank_in_wave(kj, ij, nc);
             out.append(have && r < need, ij);
         }
     }

@@ -299,3 +299,66 @@ def test_deferred_list_overflow(topk):
     assert np.all(stats[:, 0] == 6)
     bad = check_fast_raw(got, expect(wl), wl.lengths, wl.n_cols, wl.k)
     assert not bad, bad[:10]
+
+
+# ----------------------------------------------------------------------------
+# sign of the cutoff, batches past the longest-first table, tiny batches
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_negative_and_straddling_cutoffs(topk, k):
+    # Rows shifted so the cutoff key falls below +0 (all-negative rows) or
+    # right at it (about k positive scores per row): both filters then take
+    # the signed compare rather than the non-negative one.
+    rng = np.random.default_rng(31)
+    B, W = 24, 131072
+    shift = np.empty((B, 1), np.float32)
+    shift[:8] = 10.0          # every score negative
+    shift[8:16] = 2.15        # about 1.6 % positive: cutoff near zero for k = 2048
+    shift[16:] = 2.88         # about 0.2 % positive: cutoff near zero for k = 512
+    scores = (rng.standard_normal((B, W)).astype(np.float32) - shift).astype(np.float32)
+    lengths = synth.ragged_lengths(rng, B, W)
+    synth.poison_tails(scores, lengths)
+    wl = synth.Workload("negative_cutoffs", 31, scores, lengths, W, k)
+    want = expect(wl)
+    for force in (0, 2):
+        got, stats = run(topk, wl, force=force, want_stats=True)
+        assert_parity(wl, got, want)
+        say("  row paths:", dict(zip(*np.unique(stats[:, 0], return_counts=True))))
+        assert np.all(stats[:8, 0] == 3), stats[:8]
+
+
+def test_batch_above_longest_first_table(topk):
+    # 3000 rows of 8192 (above the LDS capacity): rows are claimed in batch
+    # order once the batch no longer fits the longest-first table.
+    rng = np.random.default_rng(32)
+    B, W, k = 3000, 8192, 256
+    scores = rng.standard_normal((B, W)).astype(np.float32)
+    lengths = rng.integers(0, W + 1, B).astype(np.int32)
+    lengths[::7] = W
+    synth.poison_tails(scores, lengths)
+    wl = synth.Workload("unordered_batch", 32, scores, lengths, W, k)
+    want = expect(wl)
+    for force in (0, 2):
+        got, stats = run(topk, wl, force=force, want_stats=True)
+        bad = check_fast_raw(got, want, wl.lengths, wl.n_cols, wl.k)
+        assert not bad, f"rows differing from the oracle: {bad[:10]}"
+        say("  row paths:", dict(zip(*np.unique(stats[:, 0], return_counts=True))))
+    assert_parity(wl, got, want)
+
+
+@pytest.mark.parametrize("batch", [1, 3, 255])
+def test_batches_below_the_cu_count(topk, batch):
+    # fewer rows than workgroups: most workgroups find no row to claim
+    rng = np.random.default_rng(33 + batch)
+    W, k = 262144, 2048
+    scores = rng.standard_normal((batch, W)).astype(np.float32)
+    lengths = synth.ragged_lengths(rng, batch, W)
+    synth.poison_tails(scores, lengths)
+    wl = synth.Workload(f"batch{batch}", 33, scores, lengths, W, k)
+    want = expect(wl)
+    for force in (0, 3):
+        got, stats = run(topk, wl, force=force, want_stats=True)
+        assert_parity(wl, got, want)
+        if force == 0:
+            assert np.all(stats[:, 0] == 3), stats

@@ -422,11 +422,11 @@ struct SamplePlan {
     }
 };
 
-// Scope S: loads row R's sample from HBM straight into LDS, group t at
-// skey[4t, 4t + 4) whichever scope loads it (lane l of a wave writes 16
-// bytes at the wave's LDS base + 16 l), and waits for this wave's loads.
+// Scope S: issues the loads of row R's sample from HBM straight into LDS,
+// group t at skey[4t, 4t + 4) whichever scope loads it (lane l of a wave
+// writes 16 bytes at the wave's LDS base + 16 l).
 template <class S>
-__device__ __forceinline__ void sample_load(const Params& p, Shared& sm, const RowSlot& R) {
+__device__ __forceinline__ void sample_issue(const Params& p, Shared& sm, const RowSlot& R) {
     constexpr int kPer = (kMaxSample / 4 + S::kSize - 1) / S::kSize;  // 16-byte loads per lane
     const SamplePlan plan(R.L);
     const float* row = p.scores + R.b * p.row_stride;
@@ -439,7 +439,20 @@ __device__ __forceinline__ void sample_load(const Params& p, Shared& sm, const R
                 row + plan.group_start(t),
                 (__attribute__((address_space(3))) void*)(sm.skey + 4 * (h * S::kSize + wave_base)), 16, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// An s_waitcnt immediate (vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at
+// their maxima) given to the compiler as a builtin rather than inline asm, so
+// that its own wait tracking knows the sample's LDS writes have landed and
+// adds no wait of its own for them at later LDS accesses and barriers, where
+// streaming loads may be in flight.
+constexpr unsigned kWaitVm0 = 0x0F70u;  // vmcnt(0)
+
+// The same, and waits for this wave's loads.
+template <class S>
+__device__ __forceinline__ void sample_load(const Params& p, Shared& sm, const RowSlot& R) {
+    sample_issue<S>(p, sm, R);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
 // Scope S: the cutoff of row R from the sample in LDS (see sample_cutoff).
@@ -1040,25 +1053,32 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     const uint32_t cap = (uint32_t)p.capacity;
     const SelectLds sampler_lds{sm.shist, sm.sfound};
 
-    // start: the sampler wave claims rows 0 and 1, and the whole workgroup
-    // finds row 0's cutoff (every wave loads a share of the sample) before
-    // any streaming load is issued: queued streaming loads would hold the
-    // sample's loads, and the waves issuing them, back
+    // start: the sampler wave claims rows 0 and 1; the whole workgroup
+    // loads row 0's sample (every wave a share) and finds its cutoff. Each
+    // streaming wave issues its first chunk once the sample is in, so that
+    // the chunk's latency overlaps the cutoff search; issued earlier, the
+    // chunk loads would queue ahead of the sample's.
     if (wave_id() == 1) {
         claim_row(p, sm, sm.slot[0], sampler_lds, &sm.semitted);
         claim_row(p, sm, sm.slot[1], sampler_lds, &sm.semitted);
         if (lane_id() == 0) sm.n_claimed = 2u;
     }
     B::sync();
-    if (sm.slot[0].valid && sm.slot[0].kind == kKindSampled) {
-        sample_load<B>(p, sm, sm.slot[0]);
+    const bool sampled0 = sm.slot[0].valid && sm.slot[0].kind == kKindSampled;
+    if (sampled0) sample_load<B>(p, sm, sm.slot[0]);
+    Chunk a, b;
+    Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0};
+    if (wave_id() >= kFirstStreamer) {
+        // rows 0-1 only: later rows are not claimed before the roles start
+        st.c = st.grab(st.i, 1, false);
+        st.load(a, st.i, st.c);
+    }
+    if (sampled0) {
         B::sync();
         sample_select<B>(sm, sm.slot[0], sampler_lds);
     }
     if (threadIdx.x == 0) sm.n_ready = 1u;
     B::sync();
-    Chunk a, b;
-    Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0};
 
     if (wave_id() == 0) {
         // finisher: rows in order; the last row is left to the whole workgroup
@@ -1097,9 +1117,12 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
             publish(&sm.n_claimed, (uint32_t)j + 2u);
         }
     } else {
-        st.c = st.grab(st.i, INT32_MAX, false);
-        st.load(a, st.i, st.c);
-        bool more = st.c != kEnd;
+        bool more = st.c < kNone;  // a chunk of row 0 or 1 issued at the start
+        if (!more && st.c != kEnd) {
+            st.c = st.grab(st.i, INT32_MAX, false);
+            st.load(a, st.i, st.c);
+            more = st.c != kEnd;
+        }
         while (more) {
             more = st.step(a, b);
             if (more) more = st.step(b, a);

@@ -252,8 +252,19 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
     uint32_t* cnt = sm.hist[0];
     uint32_t* start = sm.hist[1];  // rows in higher buckets
     uint32_t* fill = sm.shist;
-    for (uint32_t b = threadIdx.x; b < n; b += kThreads) {
-        const int64_t L = row_len(p, b);
+    // every length load in flight before the first is used
+    constexpr int kPer = (kOrderMaxRows + kThreads - 1) / kThreads;
+    int64_t lens[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const uint32_t b = threadIdx.x + (uint32_t)j * kThreads;
+        lens[j] = b < n ? row_len(p, b) : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const uint32_t b = threadIdx.x + (uint32_t)j * kThreads;
+        if (b >= n) break;
+        const int64_t L = lens[j];
         len[b] = (int32_t)L;
         uint32_t d = (uint32_t)kBins;
         if (L > p.k) {

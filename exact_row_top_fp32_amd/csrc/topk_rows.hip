@@ -118,9 +118,8 @@ struct Shared {
     uint32_t ncand;
     uint32_t smax;
     uint32_t slo;
-    uint32_t cand_key[kMaxCand + 64];  // the last 64: a lane's write that is not kept
-    uint32_t cand_idx[kMaxCand + 64];
-    uint32_t sink[64];                 // a lane's output word that is not kept
+    uint32_t cand_key[kMaxCand];
+    uint32_t cand_idx[kMaxCand];
     uint32_t ndeferred;
     int32_t deferred[kMaxDeferred];
     int32_t deferred_code[kMaxDeferred];
@@ -957,18 +956,24 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
             const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
             next += total & 0xFFFFu;
             ncand += total >> 16;
-            // no branch per entry: a lane's write that is not kept goes to
-            // a word of its own
+            // stores under the lane mask only: the streaming waves share the
+            // LDS, so unneeded lane writes cost them bandwidth
 #pragma unroll
             for (int j = 0; j < kU; ++j) {
                 const uint32_t tb = (tmask >> j) & 1u;
-                *(tb ? stage + ts : sm.sink + lane) = v[j].y;
+                if (tb) stage[ts] = v[j].y;
                 ts += tb;
-                const uint32_t cb = (cmask >> j) & 1u;
-                const uint32_t c_at = cb && cs < (uint32_t)kMaxCand ? cs : (uint32_t)kMaxCand + lane;
-                sm.cand_key[c_at] = val(v[j].x);
-                sm.cand_idx[c_at] = v[j].y;
-                cs += cb;
+            }
+            if ((total >> 16) != 0u) {  // a cutoff-bin candidate in this step (rare)
+#pragma unroll
+                for (int j = 0; j < kU; ++j) {
+                    const uint32_t cb = (cmask >> j) & 1u;
+                    if (cb && cs < (uint32_t)kMaxCand) {
+                        sm.cand_key[cs] = val(v[j].x);
+                        sm.cand_idx[cs] = v[j].y;
+                    }
+                    cs += cb;
+                }
             }
         }
         if (!whole) {

@@ -63,6 +63,7 @@ constexpr int kSlots = 4;                                  // rows i-1 .. i+2
 constexpr int kTable = 64;                                 // queued rows fetched at a time
 constexpr int kMaxDeferred = 64;                           // full-row rows per workgroup
 constexpr int kOrderMaxRows = 2048;                        // longest-first order up to this batch
+constexpr int kHeavyBucket = 64;                           // larger length buckets: ranked by a scan
 
 constexpr uint32_t kKindSampled = 0, kKindAll = 1, kKindFull = 2;
 constexpr uint64_t kWatchdogTicks = 10ull * 100000000ull;  // 10 s
@@ -120,6 +121,8 @@ struct Shared {
     uint32_t slo;
     uint32_t cand_key[kMaxCand];
     uint32_t cand_idx[kMaxCand];
+    uint32_t heavy[kOrderMaxRows / (kHeavyBucket + 1) + 1];  // queue buckets ranked by scans
+    uint32_t nheavy;
     uint32_t ndeferred;
     int32_t deferred[kMaxDeferred];
     int32_t deferred_code[kMaxDeferred];
@@ -286,6 +289,7 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
         for (int j = 31; j >= 0; --j) {
             start[32 * lane + j] = above;
             above += c[j];
+            if (c[j] > (uint32_t)kHeavyBucket) sm.heavy[atomicAdd(&sm.nheavy, 1u)] = 32 * lane + j;
         }
         if (lane == 0) sm.nqueue = total;
     }
@@ -300,9 +304,30 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
         const uint32_t b = placed[t];
         const uint32_t d = bucket[b];
         const uint32_t s0 = start[d], s1 = s0 + cnt[d];
+        if (s1 - s0 > (uint32_t)kHeavyBucket) continue;
         uint32_t r = 0;
         for (uint32_t u = s0; u < s1; ++u) r += placed[u] < b ? 1u : 0u;
         order[s0 + r] = b;
+    }
+    // a bucket of many rows (rows of one length, say): ranks by index from
+    // a workgroup-wide scan of "row b is in the bucket" over b
+    const uint32_t nh = sm.nheavy;
+    for (uint32_t h = 0; h < nh; ++h) {
+        const uint32_t d = sm.heavy[h];
+        const uint32_t b0 = threadIdx.x * (uint32_t)kPer;
+        uint32_t own = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) own += b0 + j < n && bucket[b0 + j] == d ? 1u : 0u;
+        const uint32_t incl = wave_inclusive_sum(own);
+        uint32_t* wave_total = fill;  // free once the rows are placed
+        B::sync();
+        if (lane_id() == 63) wave_total[wave_id()] = incl;
+        B::sync();
+        uint32_t r = start[d] + incl - own;
+        for (uint32_t w = 0; w < wave_id(); ++w) r += wave_total[w];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (b0 + j < n && bucket[b0 + j] == d) order[r++] = b0 + j;
     }
     B::sync();
     if (threadIdx.x < 64) {
@@ -325,6 +350,7 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
     const uint32_t nd = sm.ndirect;
     B::sync();
     for (int i = threadIdx.x; i < kBins; i += kThreads) cnt[i] = start[i] = fill[i] = 0u;
+    if (threadIdx.x == 0) sm.nheavy = 0u;
     for (uint32_t j = 0; j < nd; ++j) {
         const uint32_t b = direct[j];
         direct_row<B>(p, b, len[b]);
@@ -1055,6 +1081,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         sm.ncand = 0u;
         sm.ndeferred = 0u;
         sm.ndirect = 0u;
+        sm.nheavy = 0u;
         sm.n_claimed = sm.n_ready = sm.n_finished = 0u;
         sm.last_row = -1;
         sm.abort = 0u;

@@ -362,3 +362,26 @@ def test_batches_below_the_cu_count(topk, batch):
         assert_parity(wl, got, want)
         if force == 0:
             assert np.all(stats[:, 0] == 3), stats
+
+
+@pytest.mark.parametrize("layout", ["one_length", "two_lengths_and_ragged"])
+def test_rows_sharing_a_length_bucket(topk, layout):
+    # many rows of one length fall into one bucket of the longest-first sort,
+    # whose index order then comes from a workgroup-wide scan
+    rng = np.random.default_rng(34)
+    B, W, k = 700, 9000, 300
+    scores = rng.standard_normal((B, W)).astype(np.float32)
+    if layout == "one_length":
+        lengths = np.full(B, W, np.int32)
+    else:
+        lengths = rng.integers(k + 1, W + 1, B).astype(np.int32)
+        lengths[rng.permutation(B)[:250]] = W
+        lengths[rng.permutation(B)[:200]] = W // 2
+    synth.poison_tails(scores, lengths)
+    wl = synth.Workload(f"bucket_{layout}", 34, scores, lengths, W, k)
+    want = expect(wl)
+    for force in (0, 2):
+        got, stats = run(topk, wl, force=force, want_stats=True)
+        bad = check_fast_raw(got, want, wl.lengths, wl.n_cols, wl.k)
+        assert not bad, f"rows differing from the oracle: {bad[:10]}"
+    assert_parity(wl, got, want)

@@ -952,6 +952,13 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
     const uint64_t hi = (uint64_t)R.T + ((uint64_t)(f.digit + 1u) << sh);
     const uint32_t t_above = (hi > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)(hi - 1u)) - kShift;
     const uint32_t t_lo = R.T + (f.digit << sh) - kShift;  // the bin holds a survivor, so no overflow
+    // per entry: taken <=> val >= t_take (and not take_none); a candidate
+    // <=> val - t_lo <= c_span (unsigned) and candidates are wanted. Plain
+    // compares and bitwise ands, so that the entry loops have no branches.
+    const uint32_t t_take = whole ? t_lo : t_above + 1u;
+    const bool take_none = !whole && t_above == 0xFFFFFFFFu;
+    const bool want_cand = !whole;
+    const uint32_t c_span = t_above - t_lo;
     if constexpr (kWave) {
         // Selected positions are compacted in place into the buffer's first
         // words (after a step's entries are read, the selected count cannot
@@ -971,8 +978,10 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
             for (int j = 0; j < kU; ++j) {
                 const bool ok = e0 + 64 * j + lane < n;
                 const uint32_t kv = val(v[j].x);
-                tmask |= (ok && (whole ? kv >= t_lo : kv > t_above)) ? 1u << j : 0u;
-                cmask |= (ok && !whole && kv >= t_lo && kv <= t_above) ? 1u << j : 0u;
+                const bool take = ok & !take_none & (kv >= t_take);
+                const bool cand = ok & want_cand & (kv - t_lo <= c_span);
+                tmask |= (uint32_t)take << j;
+                cmask |= (uint32_t)cand << j;
             }
             const uint32_t packed = (uint32_t)__popc(tmask) | ((uint32_t)__popc(cmask) << 16);
             const uint32_t incl = wave_inclusive_sum(packed);
@@ -1019,8 +1028,8 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
         for (uint32_t e = S::rank(); e < n; e += S::kSize) {
             const uint2 v = E[e];
             const uint32_t kv = val(v.x);
-            out.append(whole ? kv >= t_lo : kv > t_above, v.y);
-            const bool cand = !whole && kv >= t_lo && kv <= t_above;
+            out.append(!take_none & (kv >= t_take), v.y);
+            const bool cand = want_cand & (kv - t_lo <= c_span);
             const uint32_t slot = wave_reserve(&sm.ncand, cand);
             if (cand && slot < (uint32_t)kMaxCand) {
                 sm.cand_key[slot] = kv;

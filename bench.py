@@ -85,6 +85,9 @@ def main() -> int:
     ap.add_argument("--only", choices=["c3", "c4"], default=None,
                     help="time one batch only (for profiling a single launch shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--small-batch", type=int, default=40,
+                    help="also time the first N rows of each batch through topk_select and the "
+                         "split-row topk_select_split (0 = skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known "
                          "read and write size for calibrating memory counters)")
@@ -202,6 +205,9 @@ def main() -> int:
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic}
 
+    small = small_batch(topk, wls, d_scores, d_len, names, args.small_batch, stream) \
+        if args.small_batch > 0 and not args.only else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wls, d_out, names)
@@ -229,10 +235,49 @@ def main() -> int:
         },
         "detail": detail,
         "roofline": roofline,
+        "small_batch": small,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def small_batch(topk, wls, d_scores, d_len, names, rows, stream, iters=200):
+    """The first `rows` rows of each batch: one workgroup per row (topk_select)
+    against rows split over several workgroups (topk_select_split), warm
+    medians of HIP events on the launch stream, and equal outputs."""
+    import torch
+
+    res = {}
+    for n in names:
+        w = wls[n]
+        s, ln = d_scores[n][:rows], d_len[n][:rows]
+        out_a = torch.empty((rows, w.k), dtype=torch.int32, device=s.device)
+        out_b = torch.empty_like(out_a)
+        ws = torch.empty(topk.topk_split_workspace_bytes(rows), dtype=torch.uint8, device=s.device)
+        L = np.clip(w.lengths[:rows].astype(np.int64), 0, w.n_cols)
+        nbytes = int(4 * L.sum() + 4 * rows + 4 * rows * w.k)
+        calls = {"topk_select": lambda: topk.topk_select(s, ln, w.k, out_a, stream=stream),
+                 "topk_select_split": lambda: topk.topk_select_split(s, ln, w.k, out_b, workspace=ws,
+                                                                     stream=stream)}
+        entry = {"rows": rows, "width": w.n_cols, "k": w.k, "algorithmic_bytes": nbytes}
+        for name, fn in calls.items():
+            for _ in range(10):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(iters)]
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+            entry[name] = {"warm_us_median": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                           "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        entry["same_selection"] = bool(torch.equal(torch.sort(out_a, 1).values, torch.sort(out_b, 1).values))
+        log(f"small batch {n}: {entry}")
+        res[n] = entry
+    return res
 
 
 CPU_TARGET_S = 10.0  # oracle wall time to aim for

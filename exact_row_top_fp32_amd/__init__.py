@@ -14,7 +14,8 @@ import os
 import torch
 
 __all__ = [
-    "topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity", "topk_watchdog_trips",
+    "topk_select", "topk_select_ex", "topk_select_split", "topk_split_workspace_bytes",
+    "topk_split_capacity", "topk_status_string", "topk_max_capacity", "topk_watchdog_trips",
     "TopKError", "library_path", "PATH_AUTO", "PATH_LDS", "PATH_SAMPLED", "PATH_FULLROW",
     "ROW_EMPTY", "ROW_ALL", "ROW_LDS", "ROW_SAMPLED", "ROW_FULL_OVERFLOW",
     "ROW_FULL_UNDERFLOW", "ROW_FULL_FORCED", "MAX_K",
@@ -63,6 +64,13 @@ def _load():
         lib.topk_max_capacity.argtypes = []
         lib.topk_watchdog_trips.restype = ctypes.c_uint32
         lib.topk_watchdog_trips.argtypes = []
+        lib.topk_select_split.restype = ctypes.c_int
+        lib.topk_select_split.argtypes = (_ARGS[:-1] + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                                         ctypes.c_void_p, ctypes.POINTER(_Options)])
+        lib.topk_split_workspace_bytes.restype = ctypes.c_int64
+        lib.topk_split_workspace_bytes.argtypes = [ctypes.c_int64]
+        lib.topk_split_capacity.restype = ctypes.c_int32
+        lib.topk_split_capacity.argtypes = []
         _lib = lib
     return _lib
 
@@ -159,4 +167,40 @@ def topk_select_ex(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
         raise ValueError("row_stats must be a contiguous [batch, 2] tensor")
     opt = _Options(int(force_path), int(capacity), _device_ptr(row_stats, "row_stats", torch.int32))
     _check(_load().topk_select_ex(*args, ctypes.byref(opt)))
+    return out
+
+
+def topk_split_workspace_bytes(batch: int) -> int:
+    """Bytes of device workspace ``topk_select_split`` needs for ``batch`` rows."""
+    return int(_load().topk_split_workspace_bytes(int(batch)))
+
+
+def topk_split_capacity() -> int:
+    """Survivor entries per row in the split-row workspace."""
+    return int(_load().topk_split_capacity())
+
+
+def topk_select_split(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
+                      out: torch.Tensor | None = None, page_table: torch.Tensor | None = None,
+                      page_size: int = 0, *, workspace: torch.Tensor | None = None, pieces: int = 0,
+                      n_cols: int | None = None, stream=None, force_path: int = PATH_AUTO,
+                      capacity: int = 0, row_stats: torch.Tensor | None = None) -> torch.Tensor:
+    """``topk_select`` with every row split over several workgroups (small batches).
+
+    Same result as ``topk_select``. ``workspace`` is a uint8 GPU tensor of at
+    least ``topk_split_workspace_bytes(batch)`` bytes (allocated here when
+    omitted); ``pieces`` is the number of workgroups per row (0 = automatic).
+    """
+    args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream)
+    if row_stats is not None and (row_stats.shape != (scores.size(0), 2) or not row_stats.is_contiguous()):
+        raise ValueError("row_stats must be a contiguous [batch, 2] tensor")
+    need = topk_split_workspace_bytes(scores.size(0))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=scores.device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    opt = _Options(int(force_path), int(capacity), _device_ptr(row_stats, "row_stats", torch.int32))
+    status = _load().topk_select_split(*args[:-1], _device_ptr(workspace, "workspace", torch.uint8),
+                                       workspace.numel(), int(pieces), args[-1], ctypes.byref(opt))
+    _check(status)
     return out

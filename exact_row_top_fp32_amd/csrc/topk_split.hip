@@ -1,0 +1,406 @@
+// Exact per-row top-k with each row split over several workgroups, for
+// batches too small to fill the chip one row per compute unit (gfx950).
+//
+// With one workgroup per row, a batch of 40 rows keeps 40 of 256 compute
+// units busy. Here every row is cut into pieces of equal size, one workgroup
+// each, so the grid fills the chip at any batch (the counterpart of the
+// cluster-split rows of "dsv4.1: Top-k kernels and candidate selection",
+// implementation section 4, where several blocks share one long row). Three
+// launches on the caller's stream, and a workspace the caller owns:
+//
+//  1. split_sample_kernel, one workgroup per row: a row with L <= k is written
+//     out directly; any other row gets its cutoff key T from a sample of the
+//     row (vLLM PR #56346 report, summary and implementation item 1: a
+//     sampled cutoff, then exact selection among the survivors) and a fresh
+//     header in the workspace.
+//  2. split_stream_kernel, one workgroup per piece: reads its piece once and
+//     appends every (raw score bits, position) with key >= T to the row's
+//     survivor area in the workspace, one device-scope reservation per wave
+//     and load round, counting on past the capacity without writing (same
+//     page, implementation item 1).
+//  3. split_finish_kernel, one workgroup per row: loads the row's survivors
+//     into LDS (all loads in flight at once) and selects the exact top m
+//     there, or, when they overflowed the area or fell short of m, runs the
+//     full-row exact selection: histogram passes down to the cutoff, then one
+//     emission scan ("Fix incorrect sparse-attention top-k selection when
+//     candidate bins overflow", comment thread: cutoff first).
+//
+// Kernel boundaries order the three steps, so no workgroup waits for another
+// and no device-scope fence is needed. The selected set is the one every
+// other path returns: all positions whose key is above the cutoff key, then
+// the lowest positions equal to it.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "exact_topk.h"
+#include "topk_device.h"
+
+namespace topk {
+namespace {
+
+constexpr int kThreads = 256;                   // 4 waves per workgroup
+constexpr int kUnroll = 8;                      // 16-byte loads per lane per round
+constexpr int64_t kRound = kThreads * kUnroll;  // 4-score groups per workgroup round (32 KB)
+constexpr int kRunLen = 64;                     // scores per contiguous sample run
+constexpr int kMaxRuns = 64;
+constexpr int kMaxSample = kRunLen * kMaxRuns;  // 4096 keys at most
+constexpr int kMaxPieces = 256;                 // workgroups per row at most
+constexpr int kFinThreads = 1024;               // finisher workgroup: 16 waves
+
+constexpr uint32_t kKindSampled = 0, kKindAll = 1, kKindFull = 2, kKindDirect = 3;
+
+// Per-row header in the workspace; the sample kernel writes all of it.
+struct SplitHead {
+    uint32_t count;  // survivors reserved (may exceed the capacity)
+    uint32_t spare;  // unused (keeps the header 16 bytes)
+    uint32_t T;      // cutoff key: survivors have key >= T
+    uint32_t kind;   // kKind*
+};
+
+struct SplitParams {
+    const float* scores;
+    int64_t row_stride;
+    int64_t n_cols;
+    const int32_t* lengths;
+    int32_t* out;
+    const int32_t* page_table;
+    int64_t pt_stride;
+    int32_t page_size;
+    int32_t k;
+    int32_t force_path;
+    int32_t capacity;  // survivor entries per row, <= kSplitCapacity
+    int32_t* row_stats;
+    int64_t batch;
+    SplitHead* head;     // [batch]
+    uint2* surv;         // [batch][kSplitCapacity]: (raw score bits, position)
+    int64_t piece_vec;   // 4-score groups per piece, a multiple of kRound
+    int32_t pieces;      // workgroups per row
+};
+
+constexpr int64_t kSplitCapacity = 8192;  // survivor entries per row in the workspace
+
+int64_t head_bytes(int64_t batch) { return (batch * (int64_t)sizeof(SplitHead) + 255) & ~(int64_t)255; }
+
+__device__ __forceinline__ int64_t split_row_len(const SplitParams& p, int64_t b) {
+    int64_t L = p.lengths ? (int64_t)p.lengths[b] : p.n_cols;
+    return L < 0 ? 0 : (L > p.n_cols ? p.n_cols : L);
+}
+
+__device__ __forceinline__ OutRow split_out_row(const SplitParams& p, int64_t b, uint32_t m, uint32_t* emitted) {
+    return OutRow{p.out + b * (int64_t)p.k, p.page_table ? p.page_table + b * p.pt_stride : nullptr,
+                  p.page_size, m, emitted};
+}
+
+__device__ __forceinline__ void split_stats(const SplitParams& p, int64_t b, int code, uint32_t seen) {
+    if (p.row_stats != nullptr) {
+        p.row_stats[2 * b + 0] = code;
+        p.row_stats[2 * b + 1] = (int32_t)seen;
+    }
+}
+
+// Keys held in an LDS array, position = array index.
+struct LdsKeys {
+    const uint32_t* key;
+    uint32_t n;
+    template <class F>
+    __device__ void for_each(F&& f) const {
+        for (uint32_t e = threadIdx.x; e < n; e += kThreads) f(key[e], e);
+    }
+};
+
+// ----------------------------------------------------------------------------
+// launch 1: direct rows, cutoffs and headers
+// ----------------------------------------------------------------------------
+
+// The want-th largest key of a sample of row b: `runs` runs of 64 contiguous
+// scores at evenly spaced offsets over [0, L). When the sample has fewer
+// than `want` keys above the row's m-th largest, fewer than m scores can be
+// at or above T; the rank is set so that this is a six-sigma event: the
+// number of sample keys at or above the m-th largest score is binomial with
+// mean mu = m n / L, and want = ceil(mu + 6 sqrt(mu) + 4).
+__device__ uint32_t split_cutoff(const SplitParams& p, int64_t b, int64_t L, uint32_t m, uint32_t* skey,
+                                 SelectLds lds) {
+    using B = BlockScope<kThreads>;
+    const int64_t fit = L / (2 * kRunLen);
+    const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
+    if (runs < 2) return 0u;  // too short to sample: keep every score
+    const int nsv = runs * (kRunLen / 4);
+    const int64_t span = L - kRunLen;
+    const float4* row = reinterpret_cast<const float4*>(p.scores + b * p.row_stride);
+    constexpr int kPer = kMaxSample / 4 / kThreads;  // groups per thread, all loads in flight
+    float4 x[kPer];
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+        const int t = h * kThreads + (int)threadIdx.x;
+        const int r = t / (kRunLen / 4);
+        // run r starts at floor(r * span / (runs - 1)), rounded down to a group
+        const int64_t start = ((int64_t)r * span / (runs - 1)) >> 2;
+        x[h] = t < nsv ? row[start + t % (kRunLen / 4)] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+        const int t = h * kThreads + (int)threadIdx.x;
+        if (t < nsv) {
+            skey[4 * t + 0] = order_key(x[h].x);
+            skey[4 * t + 1] = order_key(x[h].y);
+            skey[4 * t + 2] = order_key(x[h].z);
+            skey[4 * t + 3] = order_key(x[h].w);
+        }
+    }
+    B::sync();
+    const uint32_t n = 4u * (uint32_t)nsv;
+    const float mu = (float)m * (float)n / (float)L;
+    const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
+    if (wantf >= (float)n) return 0u;
+    const uint32_t want = (uint32_t)wantf;
+    // exact, or the lower edge of a bin whose keys are exactly the top `want`:
+    // either way at most the want-th largest sample key
+    return radix_select<B>(lds, LdsKeys{skey, n}, KeyView{}, want, 0u, 32, n).value;
+}
+
+__global__ __launch_bounds__(kThreads) void split_sample_kernel(SplitParams p) {
+    using B = BlockScope<kThreads>;
+    __shared__ uint32_t skey[kMaxSample];
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t found[3];
+    for (int i = (int)threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
+    B::sync();
+    const int64_t b = blockIdx.x;
+    const int64_t L = split_row_len(p, b);
+    const uint32_t m = (uint32_t)(L < p.k ? L : p.k);
+    uint32_t kind, T = 0u;
+    if (L <= p.k) {
+        kind = kKindDirect;
+        const OutRow out = split_out_row(p, b, m, nullptr);
+        for (int64_t i = threadIdx.x; i < p.k; i += kThreads) out.row[i] = i < L ? out.map((uint32_t)i) : -1;
+        if (threadIdx.x == 0) split_stats(p, b, L == 0 ? TOPK_ROW_EMPTY : TOPK_ROW_ALL, (uint32_t)L);
+    } else if (p.force_path == TOPK_PATH_FULLROW) {
+        kind = kKindFull;
+    } else if (p.force_path == TOPK_PATH_LDS) {
+        kind = L <= p.capacity ? kKindAll : kKindFull;
+    } else if (p.force_path == TOPK_PATH_AUTO && L <= p.capacity) {
+        kind = kKindAll;
+    } else {
+        kind = kKindSampled;
+        T = split_cutoff(p, b, L, m, skey, SelectLds{hist, found});
+    }
+    if (threadIdx.x == 0) p.head[b] = SplitHead{0u, 0u, T, kind};
+}
+
+// ----------------------------------------------------------------------------
+// launch 2: pieces append their survivors
+// ----------------------------------------------------------------------------
+
+// Survivor slots for every lane's `cnt` hits: one device-scope atomic per
+// wave; every lane of the wave must be active.
+__device__ __forceinline__ uint32_t wave_reserve_n(uint32_t* counter, uint32_t cnt) {
+    const uint32_t incl = wave_inclusive_sum(cnt);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    uint32_t base = 0u;
+    if (total != 0u) {
+        if (lane_id() == 0) base = atomicAdd(counter, total);
+        base = __builtin_amdgcn_readfirstlane(base);
+    }
+    return base + incl - cnt;
+}
+
+__device__ __forceinline__ void stream_piece(const SplitParams& p, int64_t b, int64_t L, uint32_t T, int piece,
+                                             SplitHead* h, uint2* surv, uint32_t cap) {
+    const int64_t nvec = L >> 2;
+    const int64_t g0 = (int64_t)piece * p.piece_vec;
+    const int64_t g1 = g0 + p.piece_vec < nvec ? g0 + p.piece_vec : nvec;
+    const float* row = p.scores + b * p.row_stride;
+    const f4* r4 = reinterpret_cast<const f4*>(row);
+    for (int64_t base = g0; base < g1; base += kRound) {  // uniform over the workgroup
+        f4 x[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t g = base + u * kThreads + threadIdx.x;
+            x[u] = g < g1 ? load_nt(r4 + g) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        uint32_t cnt = 0u;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const bool in = base + u * kThreads + threadIdx.x < g1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cnt += (in && order_key(x[u][j]) >= T) ? 1u : 0u;
+        }
+        uint32_t slot = wave_reserve_n(&h->count, cnt);
+        if (cnt != 0u) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t g = base + u * kThreads + threadIdx.x;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (g < g1 && order_key(x[u][j]) >= T) {
+                        if (slot < cap) surv[slot] = make_uint2(__float_as_uint(x[u][j]), (uint32_t)(4 * g + j));
+                        ++slot;
+                    }
+                }
+            }
+        }
+    }
+    // the L % 4 scores past the last full group belong to the piece holding
+    // that group's successor; its first wave appends them
+    if (nvec * 4 < L && nvec / p.piece_vec == piece && threadIdx.x < 64) {
+        const int64_t i = nvec * 4 + threadIdx.x;
+        const float v = i < L ? row[i] : 0.0f;
+        const bool hit = i < L && order_key(v) >= T;
+        const uint32_t slot = wave_reserve_n(&h->count, hit ? 1u : 0u);
+        if (hit && slot < cap) surv[slot] = make_uint2(__float_as_uint(v), (uint32_t)i);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void split_stream_kernel(SplitParams p) {
+    const int64_t b = blockIdx.x / (uint32_t)p.pieces;
+    const int piece = (int)(blockIdx.x % (uint32_t)p.pieces);
+    SplitHead* h = p.head + b;
+    const uint32_t kind = h->kind;
+    if (kind == kKindDirect || kind == kKindFull) return;
+    stream_piece(p, b, split_row_len(p, b), h->T, piece, h, p.surv + b * kSplitCapacity, (uint32_t)p.capacity);
+}
+
+// launch 3: the exact top m of each row
+__global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p) {
+    using B = BlockScope<kFinThreads>;
+    __shared__ uint2 lsurv[kSplitCapacity];
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t found[3];
+    __shared__ uint32_t emitted;
+    const int64_t b = blockIdx.x;
+    const SplitHead head = p.head[b];
+    if (head.kind == kKindDirect) return;
+    for (int i = (int)threadIdx.x; i < kBins; i += kFinThreads) hist[i] = 0u;
+    if (threadIdx.x == 0) emitted = 0u;
+    const int64_t L = split_row_len(p, b);
+    const uint32_t m = (uint32_t)(L < p.k ? L : p.k);
+    const uint32_t n = head.count;
+    const uint32_t cap = (uint32_t)p.capacity;
+    const SelectLds lds{hist, found};
+    OutRow out = split_out_row(p, b, m, &emitted);
+    int code;
+    if (head.kind == kKindFull || n > cap || n < m) {
+        code = head.kind == kKindFull ? TOPK_ROW_FULL_FORCED : (n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW);
+        B::sync();
+        const RowSource<B> src{p.scores + b * p.row_stride, L};
+        const Selection s = select_top<B>(lds, src, m, (uint32_t)L, 0u, 0xFFFFFFFFu, bits_for(L));
+        emit(src, s, out);
+    } else {
+        code = head.kind == kKindAll ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
+        // survivors in 16-byte pairs; an odd count reads one unused entry
+        // past it, still inside the row's area (n < capacity <= area)
+        constexpr int kPer = (int)(kSplitCapacity / 2 / kFinThreads);
+        const uint4* g4 = reinterpret_cast<const uint4*>(p.surv + b * kSplitCapacity);
+        uint4* l4 = reinterpret_cast<uint4*>(lsurv);
+        const uint32_t npair = (n + 1u) / 2u;
+        uint4 v[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const uint32_t i = (uint32_t)(q * kFinThreads) + threadIdx.x;
+            v[q] = i < npair ? g4[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const uint32_t i = (uint32_t)(q * kFinThreads) + threadIdx.x;
+            if (i < npair) l4[i] = v[q];
+        }
+        B::sync();
+        const PairSource<B> src{lsurv, n};
+        const Selection s = select_top<B>(lds, src, m, n, head.T, 0xFFFFFFFFu, bits_for(L));
+        emit(src, s, out);
+    }
+    if (threadIdx.x == 0) split_stats(p, b, code, head.kind == kKindFull ? (uint32_t)L : n);
+}
+
+int split_device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 64) {
+        const int v = cached[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace
+}  // namespace topk
+
+using namespace topk;
+
+extern "C" {
+
+int64_t topk_split_workspace_bytes(int64_t batch) {
+    if (batch < 0 || batch > INT32_MAX) return -1;
+    return head_bytes(batch) + batch * kSplitCapacity * (int64_t)sizeof(uint2);
+}
+
+int32_t topk_split_capacity(void) { return (int32_t)kSplitCapacity; }
+
+int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                      const int32_t* lengths, int32_t k, int32_t* out_idx,
+                      const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                      void* workspace, int64_t workspace_bytes, int32_t pieces, void* hip_stream,
+                      const topk_options* options) {
+    if (batch < 0 || batch > INT32_MAX) return TOPK_ERR_ARG;
+    if (k < 1 || k > TOPK_MAX_K) return TOPK_ERR_K;
+    if (n_cols < 0 || n_cols > INT32_MAX || row_stride < n_cols) return TOPK_ERR_ARG;
+    if (pieces < 0 || pieces > kMaxPieces) return TOPK_ERR_ARG;
+    topk_options opt{TOPK_PATH_AUTO, 0, nullptr};
+    if (options != nullptr) opt = *options;
+    if (opt.force_path < TOPK_PATH_AUTO || opt.force_path > TOPK_PATH_FULLROW) return TOPK_ERR_ARG;
+    if (opt.capacity < 0 || opt.capacity > kSplitCapacity) return TOPK_ERR_ARG;
+    if (opt.capacity == 0) opt.capacity = (int32_t)kSplitCapacity;
+    if (page_table != nullptr) {
+        if (page_size < 1) return TOPK_ERR_ARG;
+        if (page_table_stride < (n_cols + page_size - 1) / page_size) return TOPK_ERR_ARG;
+    }
+    if (batch == 0) return TOPK_OK;
+    if (scores == nullptr || out_idx == nullptr || workspace == nullptr) return TOPK_ERR_ARG;
+    if (workspace_bytes < topk_split_workspace_bytes(batch)) return TOPK_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(scores) & 15u) != 0) return TOPK_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TOPK_ERR_ALIGN;
+    if (batch > 1 && (row_stride & 3) != 0) return TOPK_ERR_ALIGN;
+    // pieces per row: enough workgroups for about four per compute unit, each
+    // piece a whole number of load rounds
+    int64_t want = pieces;
+    if (want == 0) {
+        const int cus = split_device_cus();
+        if (cus <= 0) return TOPK_ERR_LAUNCH;
+        want = (4 * (int64_t)cus + batch - 1) / batch;
+    }
+    const int64_t nvec_max = (n_cols + 3) / 4;
+    if (want > kMaxPieces) want = kMaxPieces;
+    if (want < 1) want = 1;
+    int64_t per = (nvec_max + want - 1) / want;
+    per = (per + kRound - 1) / kRound * kRound;
+    if (per < kRound) per = kRound;
+    const int64_t P = nvec_max > 0 ? (nvec_max + per - 1) / per : 1;
+    if (batch * P * kThreads > (int64_t)UINT32_MAX) return TOPK_ERR_ARG;
+
+    char* ws = static_cast<char*>(workspace);
+    SplitParams p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride, page_size, k,
+                  opt.force_path, opt.capacity, opt.row_stats, batch,
+                  reinterpret_cast<SplitHead*>(ws), reinterpret_cast<uint2*>(ws + head_bytes(batch)),
+                  per, (int32_t)P};
+    void* args[] = {&p};
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&split_sample_kernel), dim3((uint32_t)batch), dim3(kThreads),
+                        args, 0, st) != hipSuccess)
+        return TOPK_ERR_LAUNCH;
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&split_stream_kernel), dim3((uint32_t)(batch * P)),
+                        dim3(kThreads), args, 0, st) != hipSuccess)
+        return TOPK_ERR_LAUNCH;
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&split_finish_kernel), dim3((uint32_t)batch),
+                        dim3(kFinThreads), args, 0, st) != hipSuccess)
+        return TOPK_ERR_LAUNCH;
+    return TOPK_OK;
+}
+
+}  // extern "C"

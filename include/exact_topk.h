@@ -139,6 +139,53 @@ int32_t topk_max_capacity(void);
  */
 uint32_t topk_watchdog_trips(void);
 
+/*
+ * Split-row mode, for batches with fewer rows than the GPU has compute units
+ * (the cluster-split rows of "dsv4.1: Top-k kernels and candidate selection",
+ * implementation section 4, where several blocks share one long row).
+ * Same result as topk_select, bit for bit and index for index; each row is
+ * cut into pieces of equal size, one workgroup each, so a small batch still
+ * reads with the whole chip. Three launches on `hip_stream`:
+ *  1. one workgroup per row writes rows with L <= k directly and finds the
+ *     other rows' sampled cutoff keys;
+ *  2. one workgroup per piece appends the piece's scores at or above the
+ *     cutoff to the row's area of `workspace`;
+ *  3. one workgroup per row selects the exact top m from there, or runs the
+ *     full-row exact selection when the survivors overflow the area (the
+ *     capacity) or fall short of m.
+ *
+ *  workspace        device memory owned by the caller, 256-byte aligned,
+ *                   at least topk_split_workspace_bytes(batch) bytes; its
+ *                   contents need no initialisation and are scratch between
+ *                   calls. Calls that overlap in time must not share one.
+ *  workspace_bytes  its size in bytes
+ *  pieces           workgroups per row wanted, 0 = about four workgroups per
+ *                   compute unit over the batch, at most 256; each piece is a
+ *                   whole number of 8192-score rounds, so short rows get
+ *                   fewer pieces
+ *  options          as for topk_select_ex, with capacity up to
+ *                   topk_split_capacity(); TOPK_PATH_LDS keeps every score of
+ *                   rows up to the capacity (others take the full-row path);
+ *                   row_stats codes as for topk_select_ex (TOPK_ROW_LDS: every
+ *                   score was kept). NULL = automatic.
+ * Other arguments, results and status codes as for topk_select;
+ * TOPK_ERR_ARG also for a NULL or too small workspace, and TOPK_ERR_ALIGN for
+ * a workspace that is not 256-byte aligned.
+ */
+int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                      const int32_t* lengths, int32_t k, int32_t* out_idx,
+                      const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                      void* workspace, int64_t workspace_bytes, int32_t pieces, void* hip_stream,
+                      const topk_options* options);
+
+/* Workspace bytes topk_select_split needs for `batch` rows (-1 if batch is
+ * negative or above INT32_MAX): a 16-byte header per row, then
+ * topk_split_capacity() 8-byte survivor entries per row. */
+int64_t topk_split_workspace_bytes(int64_t batch);
+
+/* Survivor entries per row in the split-row workspace (8192). */
+int32_t topk_split_capacity(void);
+
 #ifdef __cplusplus
 }
 #endif

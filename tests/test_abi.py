@@ -48,13 +48,20 @@ def lib():
     lib.topk_select_ex.restype = ctypes.c_int
     lib.topk_status_string.restype = ctypes.c_char_p
     lib.topk_max_capacity.restype = ctypes.c_int32
+    lib.topk_select_split.argtypes = ARGS[:-1] + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                                   ctypes.c_void_p, ctypes.POINTER(Options)]
+    lib.topk_select_split.restype = ctypes.c_int
+    lib.topk_split_workspace_bytes.argtypes = [ctypes.c_int64]
+    lib.topk_split_workspace_bytes.restype = ctypes.c_int64
+    lib.topk_split_capacity.restype = ctypes.c_int32
     return lib
 
 
 def test_header_declares_the_entry_points():
     assert header_functions() == sorted(
         ["topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity",
-         "topk_watchdog_trips"])
+         "topk_watchdog_trips", "topk_select_split", "topk_split_workspace_bytes",
+         "topk_split_capacity"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -106,3 +113,49 @@ def test_status_strings(lib):
     for code in (0, 1, 2, 3, 5, 99):
         assert lib.topk_status_string(code)
     assert lib.topk_max_capacity() >= 4096
+
+
+WS = 0x100000  # 256-byte aligned, never dereferenced
+
+
+def split_call(lib, scores=FAKE, batch=4, row_stride=1024, n_cols=1024, lengths=None, k=16,
+               out=FAKE, page_table=None, pt_stride=0, page_size=0, ws=WS, ws_bytes=None,
+               pieces=0, opt=None):
+    if ws_bytes is None:
+        ws_bytes = lib.topk_split_workspace_bytes(batch) if batch >= 0 else 0
+    a = (scores, batch, row_stride, n_cols, lengths, k, out, page_table, pt_stride, page_size,
+         ws, ws_bytes, pieces, None)
+    return lib.topk_select_split(*a, ctypes.byref(opt) if opt is not None else None)
+
+
+def test_split_workspace_size(lib):
+    cap = lib.topk_split_capacity()
+    assert cap >= lib.topk_max_capacity()
+    assert lib.topk_split_workspace_bytes(0) == 0
+    assert lib.topk_split_workspace_bytes(1) == 256 + 8 * cap
+    assert lib.topk_split_workspace_bytes(40) == 768 + 40 * 8 * cap
+    assert lib.topk_split_workspace_bytes(-1) == -1 and lib.topk_split_workspace_bytes(2**31) == -1
+
+
+def test_split_host_argument_checks(lib):
+    assert split_call(lib, k=0) == 2 and split_call(lib, k=2049) == 2
+    assert split_call(lib, batch=-1) == 1 and split_call(lib, batch=2**31) == 1
+    assert split_call(lib, row_stride=1000, n_cols=1024) == 1
+    assert split_call(lib, scores=None) == 1 and split_call(lib, out=None) == 1
+    assert split_call(lib, ws=None) == 1
+    need = lib.topk_split_workspace_bytes(4)
+    assert split_call(lib, ws_bytes=need - 1) == 1
+    assert split_call(lib, ws=WS + 8) == 3
+    assert split_call(lib, scores=FAKE + 4) == 3
+    assert split_call(lib, row_stride=1026, n_cols=1024) == 3
+    assert split_call(lib, pieces=-1) == 1 and split_call(lib, pieces=257) == 1
+    assert split_call(lib, page_table=FAKE, page_size=0, pt_stride=64) == 1
+    assert split_call(lib, opt=Options(4, 0, None)) == 1
+    assert split_call(lib, opt=Options(0, lib.topk_split_capacity() + 1, None)) == 1
+    # a grid past 2^32 work-items
+    assert split_call(lib, batch=2**24, n_cols=2**31 - 1, row_stride=2**31, ws_bytes=2**62,
+                      pieces=256) == 1
+
+
+def test_split_empty_batch_is_a_no_op(lib):
+    assert split_call(lib, batch=0, scores=None, out=None, ws=None, ws_bytes=0) == 0

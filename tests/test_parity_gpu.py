@@ -119,16 +119,6 @@ def test_c2_small_capacity_forces_overflow(topk, c2):
     assert np.all(stats[:, 0] >= 4), "every row must fall back when m exceeds the capacity"
 
 
-@pytest.fixture(scope="session")
-def c3():
-    return synth.c3()
-
-
-@pytest.fixture(scope="session")
-def c4():
-    return synth.c4()
-
-
 def test_c3_decode_batch_all_rows(topk, c3):
     got, stats = run(topk, c3, want_stats=True)
     want = expect(c3)

@@ -244,8 +244,10 @@ def main() -> int:
 
 def small_batch(topk, wls, d_scores, d_len, names, rows, stream, iters=200):
     """The first `rows` rows of each batch: one workgroup per row (topk_select)
-    against rows split over several workgroups (topk_select_split), warm
-    medians of HIP events on the launch stream, and equal outputs."""
+    against rows split over several workgroups (topk_select_split), eager and
+    replayed from a HIP graph; warm medians of HIP events on the launch
+    stream, and equal outputs (the graph's last replay against the eager
+    topk_select)."""
     import torch
 
     res = {}
@@ -274,6 +276,30 @@ def small_batch(topk, wls, d_scores, d_len, names, rows, stream, iters=200):
             us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
             entry[name] = {"warm_us_median": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
                            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        # the split call's three launches captured once and replayed
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            topk.topk_select_split(s, ln, w.k, out_b, workspace=ws)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            topk.topk_select_split(s, ln, w.k, out_b, workspace=ws)
+        torch.cuda.synchronize()
+        out_b.fill_(-1)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for a, b in ev:
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        entry["topk_select_split_graph_replay"] = {
+            "warm_us_median": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del g
         entry["same_selection"] = bool(torch.equal(torch.sort(out_a, 1).values, torch.sort(out_b, 1).values))
         log(f"small batch {n}: {entry}")
         res[n] = entry

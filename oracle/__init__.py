@@ -19,6 +19,17 @@ sparse-attention top-k selection when candidate bins overflow" (sglang PR
   in paged mode), slots ``[m, k)`` get ``-1``.
 
 NaN inside ``[0, L)`` is outside the contract and raises ``ValueError``.
+
+Three more definitions, from the same sglang report (implementation section 2
+and code excerpts), for the kernels that sit beside this selection:
+
+* ``topk_bf16``: the same selection over bf16 scores (rows of at most 16384,
+  k at most 2048); a bf16 value widens exactly to the fp32 whose top 16 bits
+  it is, and the fp32 definition above applies to the widened row;
+* ``amax8``: the two-level indexer's level-one keys, the largest of every 8
+  scores, the newest block +inf, rows with at most ``topk`` blocks untouched;
+* ``sort_candidate_blocks``: the selected block ids of a row in ascending
+  order, with their pool slots.
 """
 from __future__ import annotations
 
@@ -111,3 +122,114 @@ def timed_topk(*args, **kwargs):
     t0 = time.perf_counter()
     out = topk(*args, **kwargs)
     return out, time.perf_counter() - t0
+
+
+# ----------------------------------------------------------------------------
+# bf16 rows
+# ----------------------------------------------------------------------------
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> the fp32 values they denote, exactly: a
+    bf16 number is the fp32 number whose low 16 bits are zero."""
+    bits = np.asarray(bits)
+    if bits.dtype != np.uint16:
+        raise ValueError("bf16 rows are passed as their uint16 bit patterns")
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def topk_bf16(bits: np.ndarray, lengths, k: int, *, n_cols: int | None = None,
+              page_table: np.ndarray | None = None, page_size: int = 0,
+              threads: int = 0) -> np.ndarray:
+    """Exact top-k of bf16 rows ("dsv4.1: Top-k kernels and candidate
+    selection", code excerpts, docstring of the bf16 small-row entry: the k
+    best of the first lengths[b] scores, -1 past min(k, lengths[b]), page-table
+    transform, at most 16384 scores per row and k at most 2048).
+
+    ``bits`` is uint16 ``[batch, row_stride]``; the rows are widened exactly to
+    fp32 and selected by ``topk``, so the order, the tie rule and the length
+    clamp are the fp32 ones.
+    """
+    if n_cols is None:
+        n_cols = bits.shape[1]
+    if n_cols > 16384 or not 1 <= k <= 2048:
+        raise ValueError("bf16 rows hold at most 16384 scores and k is at most 2048")
+    return topk(bf16_to_f32(bits), lengths, k, n_cols=n_cols, page_table=page_table,
+                page_size=page_size, threads=threads)
+
+
+# ----------------------------------------------------------------------------
+# the two-level indexer's neighbours
+# ----------------------------------------------------------------------------
+
+def _block_max(blocks: np.ndarray) -> np.ndarray:
+    """Largest of each row of ``blocks`` (float32 [n, 8]): NaN ignored, +0
+    above -0; NaN for a block of NaN only."""
+    nan = np.isnan(blocks)
+    top = np.where(nan, np.float32(-np.inf), blocks).max(axis=1)
+    pos_zero = ((blocks == 0) & ~np.signbit(blocks)).any(axis=1)
+    top = np.where(top == 0, np.where(pos_zero, np.float32(0.0), np.float32(-0.0)), top)
+    return np.where(nan.all(axis=1), np.float32(np.nan), top).astype(np.float32)
+
+
+def amax8(scores: np.ndarray, lengths, topk: int, out: np.ndarray) -> np.ndarray:
+    """Level-one keys of the two-level indexer ("dsv4.1: Top-k kernels and
+    candidate selection", implementation section 2, block-max kernel, and
+    code excerpts, docstring of amax8_varlen), written into ``out`` in place.
+
+    Per row b, with L = max(lengths[b], 0) and nb = ceil(L / 8) blocks:
+    ``out[b, i]`` = the largest of ``scores[b, 8i : 8i + 8]`` for i < nb - 1
+    (NaN ignored, +0 above -0; NaN only for an all-NaN block),
+    ``out[b, nb - 1] = +inf`` (the newest block is always selected), and
+    nothing is written past nb. With ``topk > 0``, a row with nb <= topk is
+    left untouched (all its blocks are selected anyway). Every L must satisfy
+    nb <= out.shape[1] and L <= scores.shape[1].
+    """
+    scores = np.asarray(scores, dtype=np.float32)
+    for b in range(scores.shape[0]):
+        L = max(int(lengths[b]), 0)
+        nb = -(-L // 8)
+        if nb > out.shape[1] or L > scores.shape[1]:
+            raise ValueError("a row's blocks do not fit the output or its scores")
+        if nb == 0 or (topk > 0 and nb <= topk):
+            continue
+        if nb > 1:
+            out[b, :nb - 1] = _block_max(scores[b, :8 * (nb - 1)].reshape(nb - 1, 8))
+        out[b, nb - 1] = np.inf
+    return out
+
+
+INT32_MAX = 2**31 - 1
+
+
+def sort_candidate_blocks(blocks: np.ndarray, lengths, page_table: np.ndarray,
+                          page_size: int):
+    """The block table of the two-level indexer ("dsv4.1: Top-k kernels and
+    candidate selection", implementation section 2, candidate-block-table
+    kernel, and code excerpts, docstring of sort_candidate_blocks).
+
+    Per row b, with nb = ceil(max(lengths[b], 0) / 8) and k = blocks.shape[1]:
+    if nb <= k the table is the identity 0 .. nb-1 whatever the input;
+    otherwise it is the distinct ids among the row's k entries that lie in
+    [0, nb), ascending (for a top-k selection that is all k of them). Slots
+    past the table hold INT32_MAX. ``pages[b, j]`` is the pool slot of the
+    j-th id: ``page_table[b, id // bpp] * bpp + id % bpp`` with
+    ``bpp = page_size // 8``, INT32_MAX where the table is padded.
+    Returns ``(table, pages)``, both int32 ``[batch, k]``.
+    """
+    if page_size < 8 or page_size & (page_size - 1):
+        raise ValueError("page_size must be a power of two, at least 8")
+    bpp = page_size // 8
+    B, k = blocks.shape
+    table = np.full((B, k), INT32_MAX, dtype=np.int32)
+    pages = np.full((B, k), INT32_MAX, dtype=np.int32)
+    for b in range(B):
+        nb = -(-max(int(lengths[b]), 0) // 8)
+        if nb <= k:
+            ids = np.arange(nb, dtype=np.int64)
+        else:
+            row = blocks[b].astype(np.int64)
+            ids = np.unique(row[(row >= 0) & (row < nb)])
+        table[b, :ids.size] = ids
+        slot = page_table[b, ids // bpp].astype(np.int64) * bpp + ids % bpp
+        pages[b, :ids.size] = slot
+    return table, pages

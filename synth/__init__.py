@@ -312,3 +312,141 @@ def c5(batch: int = 256, width: int = 65536, k: int = 1024, page_size: int = 64,
     wl = Workload(name, 5, scores, lengths, width, k, page_table=page_table, page_size=page_size)
     wl.kinds = [C5_CATEGORIES[c] for c in cats]
     return wl
+
+
+# ----------------------------------------------------------------------------
+# bf16 rows and the two-level indexer's inputs
+# ----------------------------------------------------------------------------
+
+BF16_POISON = 0x7FC0  # bf16 +quiet NaN
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), rounded to nearest, ties to even;
+    NaN becomes the quiet NaN 0x7FC0."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r[np.isnan(x)] = BF16_POISON
+    return r
+
+
+def poison_tails_bf16(bits: np.ndarray, lengths: np.ndarray) -> None:
+    for b in range(bits.shape[0]):
+        L = max(int(lengths[b]), 0)
+        bits[b, L:] = BF16_POISON
+
+
+@dataclass
+class Bf16Workload:
+    name: str
+    seed: int
+    bits: np.ndarray              # uint16 [batch, row_stride]
+    lengths: np.ndarray           # int32 [batch]
+    n_cols: int
+    k: int
+    page_table: np.ndarray | None = None
+    page_size: int = 0
+
+    @property
+    def batch(self) -> int:
+        return self.bits.shape[0]
+
+
+def _page_table(rng, batch: int, width: int, page_size: int) -> np.ndarray:
+    pages = -(-width // page_size)
+    return np.stack([rng.permutation(pages) for _ in range(batch)]).astype(np.int32)
+
+
+def bf16_rows(batch: int = 1024, width: int = 16384, k: int = 2048, seed: int = 6, *,
+              paged: bool = True, page_size: int = 64) -> Bf16Workload:
+    """The bf16 consumer rows of "dsv4.1: Top-k kernels and candidate selection"
+    (implementation section 2: rows of at most 16384 scores, k at most 2048,
+    page-table output): N(0,1) rounded to bf16, lengths uniform in 80-100 % of
+    the width, a per-row permutation page table of page_size 64."""
+    rng = np.random.default_rng(seed)
+    lengths = ragged_lengths(rng, batch, width)
+    bits = to_bf16_bits(rng.standard_normal((batch, width), dtype=np.float32))
+    poison_tails_bf16(bits, lengths)
+    pt = _page_table(rng, batch, width, page_size) if paged else None
+    return Bf16Workload(f"bf16_{batch}x{width}_k{k}", seed, bits, lengths, width, k, pt,
+                        page_size if paged else 0)
+
+
+def bf16_adversarial(k: int, width: int = 16384, seed: int = 7, rows_per_kind: int = 2) -> Bf16Workload:
+    """The adversarial fp32 row kinds, rounded to bf16: rounding merges many
+    distinct values into one, so ties are heavier still."""
+    kinds = [kd for kd in C2_KINDS for _ in range(rows_per_kind)]
+    rows = np.stack([row_of_kind(kd, width, k, seed, b) for b, kd in enumerate(kinds)])
+    bits = to_bf16_bits(rows)
+    lengths = np.full(len(kinds), width, np.int32)
+    return Bf16Workload(f"bf16_adv_{len(kinds)}x{width}_k{k}", seed, bits, lengths, width, k)
+
+
+@dataclass
+class Amax8Workload:
+    name: str
+    seed: int
+    scores: np.ndarray            # float32 [batch, row_stride], row_stride % 8 == 0
+    lengths: np.ndarray           # int32 [batch]
+    out_blocks: int               # columns of the level-one key matrix
+    topk: int
+
+    @property
+    def batch(self) -> int:
+        return self.scores.shape[0]
+
+
+def amax8_rows(batch: int = 1024, width: int = 131072, topk: int = 512, seed: int = 8, *,
+               nan_rate: float = 0.0, zero_rate: float = 0.0) -> Amax8Workload:
+    """Scores of the two-level indexer's first level ("dsv4.1: Top-k kernels and
+    candidate selection", implementation section 2): N(0,1), lengths uniform in
+    80-100 % of the width; optionally NaN (ignored by the block max) and signed
+    zeros sprinkled inside the rows. Past each length: NaN poison."""
+    rng = np.random.default_rng(seed)
+    lengths = ragged_lengths(rng, batch, width)
+    scores = rng.standard_normal((batch, width), dtype=np.float32)
+    if nan_rate > 0:
+        scores[rng.random(scores.shape) < nan_rate] = np.nan
+    if zero_rate > 0:
+        z = rng.random(scores.shape) < zero_rate
+        scores[z] = np.where(rng.random(int(z.sum())) < 0.5, np.float32(0.0), np.float32(-0.0))
+    poison_tails(scores, lengths)
+    return Amax8Workload(f"amax8_{batch}x{width}", seed, scores, lengths, -(-width // 8), topk)
+
+
+@dataclass
+class BlockTableWorkload:
+    name: str
+    seed: int
+    blocks: np.ndarray            # int32 [batch, k]: selected block ids, any order, -1 padded
+    lengths: np.ndarray           # int32 [batch] token counts (blocks = ceil(L / 8))
+    page_table: np.ndarray        # int32 [batch, pages]
+    page_size: int
+
+    @property
+    def batch(self) -> int:
+        return self.blocks.shape[0]
+
+
+def candidate_blocks(batch: int = 1024, width: int = 131072, k: int = 512, seed: int = 9, *,
+                     page_size: int = 64, short_rows: bool = True) -> BlockTableWorkload:
+    """Selected block ids as a top-k over level-one keys leaves them: k distinct
+    ids of [0, ceil(L / 8)) in random order; rows with at most k blocks hold
+    whatever (the identity table applies). Page table: a per-row permutation."""
+    rng = np.random.default_rng(seed)
+    lengths = ragged_lengths(rng, batch, width)
+    if short_rows:  # some rows with at most k blocks, and idle rows
+        pick = rng.random(batch) < 0.1
+        lengths[pick] = rng.integers(-3, 8 * k + 9, int(pick.sum()))
+    blocks = np.full((batch, k), -1, np.int32)
+    for b in range(batch):
+        nb = -(-max(int(lengths[b]), 0) // 8)
+        if nb > k:
+            blocks[b] = rng.choice(nb, k, replace=False)
+        else:
+            blocks[b] = rng.integers(-1, nb + 5, k)
+    bpp = page_size // 8
+    pages = -(-(-(-width // 8)) // bpp)
+    pt = np.stack([rng.permutation(pages) for _ in range(batch)]).astype(np.int32)
+    return BlockTableWorkload(f"blocks_{batch}x{k}", seed, blocks, lengths.astype(np.int32), pt, page_size)

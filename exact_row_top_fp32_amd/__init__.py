@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "topk_select", "topk_select_ex", "topk_select_split", "topk_split_workspace_bytes",
-    "topk_split_capacity", "topk_status_string", "topk_max_capacity", "topk_watchdog_trips",
+    "topk_split_capacity", "topk_select_bf16", "amax8_varlen", "sort_candidate_blocks",
+    "topk_status_string", "topk_max_capacity", "topk_watchdog_trips",
     "TopKError", "library_path", "PATH_AUTO", "PATH_LDS", "PATH_SAMPLED", "PATH_FULLROW",
     "ROW_EMPTY", "ROW_ALL", "ROW_LDS", "ROW_SAMPLED", "ROW_FULL_OVERFLOW",
     "ROW_FULL_UNDERFLOW", "ROW_FULL_FORCED", "MAX_K",
@@ -71,6 +72,16 @@ def _load():
         lib.topk_split_workspace_bytes.argtypes = [ctypes.c_int64]
         lib.topk_split_capacity.restype = ctypes.c_int32
         lib.topk_split_capacity.argtypes = []
+        lib.topk_select_bf16.restype = ctypes.c_int
+        lib.topk_select_bf16.argtypes = _ARGS
+        lib.amax8_varlen.restype = ctypes.c_int
+        lib.amax8_varlen.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p]
+        lib.sort_candidate_blocks.restype = ctypes.c_int
+        lib.sort_candidate_blocks.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -98,7 +109,13 @@ def _device_ptr(t: torch.Tensor | None, name: str, dtype: torch.dtype):
     return t.data_ptr()
 
 
-def _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream):
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream, dtype=torch.float32):
     if scores.dim() != 2 or (scores.size(1) > 1 and scores.stride(1) != 1):
         raise ValueError("scores must be 2-D with unit column stride")
     batch = scores.size(0)
@@ -120,11 +137,9 @@ def _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream):
                 page_table.size(1) > 1 and page_table.stride(1) != 1):
             raise ValueError("page_table must be [batch, pages] with unit column stride")
         pt_stride = page_table.stride(0) if batch > 1 else page_table.size(1)
-    if stream is None:
-        stream = torch.cuda.current_stream(scores.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, scores.device)
     args = (
-        _device_ptr(scores, "scores", torch.float32), batch, row_stride, n_cols,
+        _device_ptr(scores, "scores", dtype), batch, row_stride, n_cols,
         _device_ptr(lengths, "lengths", torch.int32), int(k),
         _device_ptr(out, "out", torch.int32), _device_ptr(page_table, "page_table", torch.int32),
         pt_stride, int(page_size), handle,
@@ -204,3 +219,80 @@ def topk_select_split(scores: torch.Tensor, lengths: torch.Tensor | None, k: int
                                        workspace.numel(), int(pieces), args[-1], ctypes.byref(opt))
     _check(status)
     return out
+
+
+def topk_select_bf16(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
+                     out: torch.Tensor | None = None, page_table: torch.Tensor | None = None,
+                     page_size: int = 0, *, n_cols: int | None = None, stream=None) -> torch.Tensor:
+    """Exact top-k of bf16 rows of at most 16384 scores (``scores`` bfloat16
+    ``[batch, >= n_cols]``); same result as ``topk_select`` on the rows
+    widened to fp32."""
+    if scores.dtype != torch.bfloat16:
+        raise TypeError(f"scores must be torch.bfloat16, got {scores.dtype}")
+    args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream,
+                         dtype=torch.bfloat16)
+    _check(_load().topk_select_bf16(*args))
+    return out
+
+
+def amax8_varlen(scores: torch.Tensor, lengths: torch.Tensor | None, topk: int = 0, *,
+                 max_seqlen: int = 0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Level-one keys of the two-level indexer: ``out[b, i]`` is the largest of
+    ``scores[b, 8i : 8i + 8]`` (NaN ignored, +0 above -0) for
+    ``i < ceil(lengths[b] / 8) - 1``, ``+inf`` at the newest block, nothing
+    past it; rows with at most ``topk`` blocks are left alone (``topk=0``
+    never skips). ``out`` is ``[batch, ceil(max_seqlen / 8)]`` fp32, allocated
+    (uninitialised) when omitted; ``max_seqlen`` defaults to the width of
+    ``scores``, and lengths are clamped to it."""
+    if scores.dim() != 2 or (scores.size(1) > 1 and scores.stride(1) != 1):
+        raise ValueError("scores must be 2-D with unit column stride")
+    batch = scores.size(0)
+    n_cols = max_seqlen if max_seqlen > 0 else scores.size(1)
+    if n_cols > scores.size(1):
+        raise ValueError("max_seqlen exceeds the width of scores")
+    if out is None:
+        out = torch.empty((batch, (n_cols + 7) // 8), dtype=torch.float32, device=scores.device)
+    if out.dim() != 2 or out.size(0) != batch or (out.size(1) > 1 and out.stride(1) != 1):
+        raise ValueError("out must be [batch, blocks] with unit column stride")
+    if lengths is not None and (lengths.dim() != 1 or lengths.size(0) != batch or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous [batch] tensor")
+    row_stride = scores.stride(0) if batch > 1 else max(scores.size(1), 1)
+    out_stride = out.stride(0) if batch > 1 else out.size(1)
+    _check(_load().amax8_varlen(_device_ptr(scores, "scores", torch.float32), batch, row_stride, n_cols,
+                                _device_ptr(lengths, "lengths", torch.int32), int(topk),
+                                _device_ptr(out, "out", torch.float32), out_stride,
+                                _stream_handle(stream, scores.device)))
+    return out
+
+
+def sort_candidate_blocks(blocks: torch.Tensor, lengths: torch.Tensor | None, page_table: torch.Tensor,
+                          page_size: int, *, out_pages: torch.Tensor | None = None,
+                          n_cols: int | None = None, stream=None) -> torch.Tensor:
+    """The two-level indexer's block table, in place: ``blocks`` (int32
+    ``[batch, k]``, selected block ids in any order) becomes the ids ascending,
+    ``INT32_MAX`` padded (the identity table for rows with at most k blocks);
+    ``out_pages`` receives ``page_table[b, id // bpp] * bpp + id % bpp``,
+    ``bpp = page_size // 8``. ``n_cols`` (the largest length, in positions)
+    defaults to ``8 * page_table.size(1) * bpp``. Returns ``out_pages``."""
+    if blocks.dim() != 2 or not blocks.is_contiguous():
+        raise ValueError("blocks must be a contiguous [batch, k] tensor")
+    batch, k = blocks.shape
+    if out_pages is None:
+        out_pages = torch.empty_like(blocks)
+    if out_pages.shape != blocks.shape or not out_pages.is_contiguous():
+        raise ValueError("out_pages must be a contiguous tensor shaped like blocks")
+    if page_table.dim() != 2 or page_table.size(0) != batch or (
+            page_table.size(1) > 1 and page_table.stride(1) != 1):
+        raise ValueError("page_table must be [batch, pages] with unit column stride")
+    if lengths is not None and (lengths.dim() != 1 or lengths.size(0) != batch or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous [batch] tensor")
+    bpp = max(page_size // 8, 1)
+    if n_cols is None:
+        n_cols = 8 * page_table.size(1) * bpp
+    pt_stride = page_table.stride(0) if batch > 1 else page_table.size(1)
+    _check(_load().sort_candidate_blocks(_device_ptr(blocks, "blocks", torch.int32), batch, int(k),
+                                         _device_ptr(lengths, "lengths", torch.int32), int(n_cols),
+                                         _device_ptr(page_table, "page_table", torch.int32), pt_stride,
+                                         int(page_size), _device_ptr(out_pages, "out_pages", torch.int32),
+                                         _stream_handle(stream, blocks.device)))
+    return out_pages

@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("topk_rows.hip", "topk_split.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("topk_rows.hip", "topk_split.hip", "topk_indexer.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libexact_topk.so")
 

@@ -186,6 +186,69 @@ int64_t topk_split_workspace_bytes(int64_t batch);
 /* Survivor entries per row in the split-row workspace (8192). */
 int32_t topk_split_capacity(void);
 
+/*
+ * Exact top-k of bf16 rows ("dsv4.1: Top-k kernels and candidate selection",
+ * implementation section 2 and code excerpts, docstring of the bf16
+ * small-row top-k: rows of at most 16384 scores, k at most 2048, selection
+ * exact, -1 past min(k, lengths[b]), optional page-table transform, no NaN).
+ * The result is topk_select's on the exactly widened fp32 rows: same order
+ * (+0 above -0), same lowest-index ties, same set. One workgroup per row.
+ *
+ *  scores     bf16 bit patterns [batch, row_stride]; 16-byte aligned base
+ *             and row_stride % 8 == 0 (when batch > 1)
+ *  n_cols     at most 16384 (TOPK_ERR_ARG above)
+ * Other arguments, results and status codes as for topk_select.
+ */
+int topk_select_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                     const int32_t* lengths, int32_t k, int32_t* out_idx,
+                     const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                     void* hip_stream);
+
+/*
+ * Level-one keys of the two-level indexer (same page, implementation section
+ * 2, block-max kernel, and the amax8_varlen docstring in the code excerpts).
+ * For row b with L = clamp(lengths[b], 0, n_cols) and nb = ceil(L / 8):
+ * out[b, i] = the largest of scores[b, 8i .. 8i+7] for i < nb - 1, NaN
+ * ignored and +0 above -0 (a block of NaN only gives +qNaN 0x7FC00000);
+ * out[b, nb - 1] = +inf (the newest block is always selected); nothing is
+ * written past nb. With topk > 0 a row with nb <= topk is left untouched.
+ *
+ *  scores      fp32 [batch, row_stride]; 32-byte aligned base and
+ *              row_stride % 8 == 0 (when batch > 1)
+ *  lengths     int32 [batch] or NULL (every row n_cols)
+ *  topk        0 (never skip) or the number of blocks the caller selects
+ *  out         fp32 [batch, out_stride], out_stride >= ceil(n_cols / 8);
+ *              device memory owned by the caller
+ * Returns TOPK_OK, TOPK_ERR_ARG (sizes, topk < 0, NULL, out_stride too
+ * small), TOPK_ERR_ALIGN or TOPK_ERR_LAUNCH. Asynchronous on hip_stream.
+ */
+int amax8_varlen(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                 const int32_t* lengths, int32_t topk, float* out, int64_t out_stride,
+                 void* hip_stream);
+
+/*
+ * The candidate block table (same page, implementation section 2, candidate
+ * block table kernel, and the sort_candidate_blocks docstring). For row b with
+ * nb = ceil(clamp(lengths[b], 0, n_cols) / 8):
+ *  - nb <= k: blocks[b] becomes 0 .. nb-1, then INT32_MAX (input unread);
+ *  - otherwise: the distinct ids among blocks[b, 0..k) that lie in [0, nb),
+ *    ascending, then INT32_MAX (a top-k selection gives k distinct ids);
+ *  - out_pages[b, j] = page_table[b, id / bpp] * bpp + id % bpp for each id of
+ *    the table, bpp = page_size / 8, INT32_MAX where the table is padded.
+ *
+ *  blocks             int32 [batch, k] contiguous, rewritten in place
+ *  n_cols             largest length in positions, at most 2^21
+ *  page_table         int32 [batch, page_table_stride],
+ *                     page_table_stride >= ceil(ceil(n_cols / 8) / bpp)
+ *  page_size          a power of two, at least 8
+ *  out_pages          int32 [batch, k] contiguous
+ * Returns TOPK_OK, TOPK_ERR_ARG or TOPK_ERR_LAUNCH. Asynchronous on
+ * hip_stream. The caller keeps pool slots inside int32.
+ */
+int sort_candidate_blocks(int32_t* blocks, int64_t batch, int32_t k, const int32_t* lengths,
+                          int64_t n_cols, const int32_t* page_table, int64_t page_table_stride,
+                          int32_t page_size, int32_t* out_pages, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -171,22 +171,24 @@ def _block_max(blocks: np.ndarray) -> np.ndarray:
     return np.where(nan.all(axis=1), np.float32(np.nan), top).astype(np.float32)
 
 
-def amax8(scores: np.ndarray, lengths, topk: int, out: np.ndarray) -> np.ndarray:
+def amax8(scores: np.ndarray, lengths, topk: int, out: np.ndarray, *, n_cols: int | None = None) -> np.ndarray:
     """Level-one keys of the two-level indexer ("dsv4.1: Top-k kernels and
     candidate selection", implementation section 2, block-max kernel, and
     code excerpts, docstring of amax8_varlen), written into ``out`` in place.
 
-    Per row b, with L = max(lengths[b], 0) and nb = ceil(L / 8) blocks:
+    Per row b, with L = clamp(lengths[b], 0, n_cols) (n_cols defaults to the
+    width of ``scores``) and nb = ceil(L / 8) blocks:
     ``out[b, i]`` = the largest of ``scores[b, 8i : 8i + 8]`` for i < nb - 1
     (NaN ignored, +0 above -0; NaN only for an all-NaN block),
     ``out[b, nb - 1] = +inf`` (the newest block is always selected), and
     nothing is written past nb. With ``topk > 0``, a row with nb <= topk is
-    left untouched (all its blocks are selected anyway). Every L must satisfy
-    nb <= out.shape[1] and L <= scores.shape[1].
+    left untouched (all its blocks are selected anyway). ``out`` needs at
+    least ceil(n_cols / 8) columns.
     """
     scores = np.asarray(scores, dtype=np.float32)
+    n_cols = scores.shape[1] if n_cols is None else n_cols
     for b in range(scores.shape[0]):
-        L = max(int(lengths[b]), 0)
+        L = min(max(int(lengths[b]), 0), n_cols)
         nb = -(-L // 8)
         if nb > out.shape[1] or L > scores.shape[1]:
             raise ValueError("a row's blocks do not fit the output or its scores")

@@ -32,7 +32,8 @@ def header_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names += re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(topk_\w+)\s*\(", text, flags=re.M)
+        names += re.findall(r"^(?:const\s+)?(?:int|int32_t|int64_t|uint32_t|char)\s*\*?\s*(\w+)\s*\(",
+                            text, flags=re.M)
     return sorted(set(names))
 
 
@@ -61,7 +62,7 @@ def test_header_declares_the_entry_points():
     assert header_functions() == sorted(
         ["topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity",
          "topk_watchdog_trips", "topk_select_split", "topk_split_workspace_bytes",
-         "topk_split_capacity"])
+         "topk_split_capacity", "topk_select_bf16", "amax8_varlen", "sort_candidate_blocks"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -159,3 +160,31 @@ def test_split_host_argument_checks(lib):
 
 def test_split_empty_batch_is_a_no_op(lib):
     assert split_call(lib, batch=0, scores=None, out=None, ws=None, ws_bytes=0) == 0
+
+
+def test_indexer_host_argument_checks(lib):
+    lib.topk_select_bf16.argtypes = ARGS
+    bf = lambda **kw: lib.topk_select_bf16(*{**dict(zip(
+        ["s", "batch", "stride", "n_cols", "len", "k", "out", "pt", "pts", "ps", "st"],
+        [FAKE, 4, 1024, 1024, None, 16, FAKE, None, 0, 0, None])), **kw}.values())
+    assert bf(n_cols=16385, stride=16392) == 1 and bf(k=2049) == 2 and bf(k=0) == 2
+    assert bf(s=FAKE + 2) == 3 and bf(stride=1028) == 3 and bf(out=None) == 1
+    assert bf(batch=0, s=None, out=None) == 0
+
+    lib.amax8_varlen.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_void_p]
+    am = lambda s=FAKE, batch=4, stride=1024, n=1024, topk=0, out=FAKE, ostride=128: lib.amax8_varlen(
+        s, batch, stride, n, None, topk, out, ostride, None)
+    assert am(ostride=127) == 1 and am(topk=-1) == 1 and am(s=None) == 1
+    assert am(s=FAKE + 16) == 3 and am(stride=1028, n=1020) == 3
+    assert am(batch=0, s=None, out=None) == 0
+
+    lib.sort_candidate_blocks.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    sb = lambda blocks=FAKE, batch=4, k=64, n=8192, pt=FAKE, pts=128, ps=64, out=FAKE: \
+        lib.sort_candidate_blocks(blocks, batch, k, None, n, pt, pts, ps, out, None)
+    assert sb(ps=48) == 1 and sb(ps=4) == 1 and sb(pts=127) == 1 and sb(k=0) == 1
+    assert sb(n=2**21 + 1, pts=2**20) == 1 and sb(pt=None) == 1 and sb(out=None) == 1
+    assert sb(batch=0, blocks=None, pt=None, out=None) == 0

@@ -85,6 +85,8 @@ def main() -> int:
     ap.add_argument("--only", choices=["c3", "c4"], default=None,
                     help="time one batch only (for profiling a single launch shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-indexer", action="store_true",
+                    help="skip timing the bf16 top-k, block-max and block-table kernels")
     ap.add_argument("--small-batch", type=int, default=40,
                     help="also time the first N rows of each batch through topk_select and the "
                          "split-row topk_select_split (0 = skip)")
@@ -208,6 +210,9 @@ def main() -> int:
     small = small_batch(topk, wls, d_scores, d_len, names, args.small_batch, stream) \
         if args.small_batch > 0 and not args.only else None
 
+    indexer = indexer_kernels(topk, wls, d_scores, d_len, stream) \
+        if not args.no_indexer and not args.only else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wls, d_out, names)
@@ -236,6 +241,7 @@ def main() -> int:
         "detail": detail,
         "roofline": roofline,
         "small_batch": small,
+        "indexer": indexer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -303,6 +309,100 @@ def small_batch(topk, wls, d_scores, d_len, names, rows, stream, iters=200):
         entry["same_selection"] = bool(torch.equal(torch.sort(out_a, 1).values, torch.sort(out_b, 1).values))
         log(f"small batch {n}: {entry}")
         res[n] = entry
+    return res
+
+
+def time_us(fn, stream, iters=100, warmup=10):
+    """Median of HIP events around `fn` on the launch stream, in µs."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+
+def rate(nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"warm_us_median": round(us, 2), "algorithmic_bytes": int(nbytes), "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def indexer_kernels(topk, wls, d_scores, d_len, stream):
+    """The kernels beside the fp32 selection, each on its own stream-ordered
+    launches: bf16 top-k over 1024 x 16384 consumer rows (k=2048, paged,
+    page_size 64), and the two-level indexer over the 128K decode batch
+    (block max with topk=512 -> fp32 top-k of 512 blocks over the block keys
+    -> block table, page_size 64), each step and the chain."""
+    import torch
+
+    import synth
+
+    dev = d_scores[next(iter(d_scores))].device
+    res = {}
+    # bf16 consumer rows
+    wb = synth.bf16_rows()
+    s = torch.from_numpy(wb.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    ln = torch.from_numpy(wb.lengths).to(dev)
+    pt = torch.from_numpy(wb.page_table).to(dev)
+    out = torch.empty((wb.batch, wb.k), dtype=torch.int32, device=dev)
+    L = np.clip(wb.lengths.astype(np.int64), 0, wb.n_cols)
+    m = np.minimum(L, wb.k)
+    nbytes = 2 * L.sum() + 4 * wb.batch + 4 * wb.batch * wb.k + 4 * np.minimum(m, -(-L // wb.page_size)).sum()
+    us = time_us(lambda: topk.topk_select_bf16(s, ln, wb.k, out, pt, wb.page_size, stream=stream), stream)
+    res["bf16_topk_1024x16384_k2048_paged"] = rate(nbytes, us)
+    log(f"indexer bf16: {res['bf16_topk_1024x16384_k2048_paged']}")
+    del s, ln, pt, out
+
+    if "c3" not in wls:
+        return res
+    w = wls["c3"]
+    k, ps = 512, 64
+    sc, ln = d_scores["c3"], d_len["c3"]
+    nblk = w.n_cols // 8
+    L = np.clip(w.lengths.astype(np.int64), 0, w.n_cols)
+    nb_h = (L + 7) // 8
+    nb = torch.from_numpy(nb_h.astype(np.int32)).to(dev)
+    keys = torch.empty((w.batch, nblk), dtype=torch.float32, device=dev)
+    sel = torch.empty((w.batch, k), dtype=torch.int32, device=dev)
+    blocks = torch.empty_like(sel)
+    pages = torch.empty_like(sel)
+    rng = np.random.default_rng(10)
+    bpp = ps // 8
+    ptab = torch.from_numpy(np.stack([rng.permutation(nblk // bpp) for _ in range(w.batch)]).astype(np.int32)).to(dev)
+    amax_bytes = (32 * np.maximum(nb_h - 1, 0) + 4 * nb_h).sum() + 4 * w.batch
+    mk = np.minimum(nb_h, k)
+    sel_bytes = 4 * nb_h.sum() + 4 * w.batch + 4 * w.batch * k
+    tab_bytes = 4 * w.batch * k + 4 * w.batch + 8 * w.batch * k + 4 * np.minimum(mk, -(-nb_h // bpp)).sum()
+
+    def step_amax():
+        topk.amax8_varlen(sc, ln, k, out=keys, stream=stream)
+
+    def step_select():
+        topk.topk_select(keys, nb, k, sel, stream=stream)
+
+    def step_table():
+        blocks.copy_(sel)
+        topk.sort_candidate_blocks(blocks, ln, ptab, ps, out_pages=pages, n_cols=w.n_cols, stream=stream)
+
+    def chain():
+        step_amax()
+        topk.topk_select(keys, nb, k, blocks, stream=stream)
+        topk.sort_candidate_blocks(blocks, ln, ptab, ps, out_pages=pages, n_cols=w.n_cols, stream=stream)
+
+    chain()
+    res["amax8_1024x131072"] = rate(amax_bytes, time_us(step_amax, stream))
+    res["topk_select_block_keys_1024x16384_k512"] = rate(sel_bytes, time_us(step_select, stream))
+    copy_us = time_us(lambda: blocks.copy_(sel), stream)
+    table_us = time_us(step_table, stream) - copy_us
+    res["block_table_1024_k512"] = rate(tab_bytes, table_us)
+    res["two_level_chain_1024x131072"] = rate(amax_bytes + sel_bytes + tab_bytes, time_us(chain, stream))
+    log(f"indexer two-level: {res}")
     return res
 
 

@@ -338,7 +338,9 @@ def indexer_kernels(topk, wls, d_scores, d_len, stream):
     launches: bf16 top-k over 1024 x 16384 consumer rows (k=2048, paged,
     page_size 64), and the two-level indexer over the 128K decode batch
     (block max with topk=512 -> fp32 top-k of 512 blocks over the block keys
-    -> block table, page_size 64), each step and the chain."""
+    -> block table, page_size 64), each step and the chain. The block keys are
+    selected both ways, one workgroup per row and split; the chain uses the
+    split entry."""
     import torch
 
     import synth
@@ -383,21 +385,28 @@ def indexer_kernels(topk, wls, d_scores, d_len, stream):
     def step_amax():
         topk.amax8_varlen(sc, ln, k, out=keys, stream=stream)
 
+    ws = torch.empty(topk.topk_split_workspace_bytes(w.batch), dtype=torch.uint8, device=dev)
+
     def step_select():
         topk.topk_select(keys, nb, k, sel, stream=stream)
+
+    def step_select_split():
+        topk.topk_select_split(keys, nb, k, sel, workspace=ws, stream=stream)
 
     def step_table():
         blocks.copy_(sel)
         topk.sort_candidate_blocks(blocks, ln, ptab, ps, out_pages=pages, n_cols=w.n_cols, stream=stream)
 
     def chain():
+        # short rows (16384 block keys): the split-row entry selects them faster
         step_amax()
-        topk.topk_select(keys, nb, k, blocks, stream=stream)
+        topk.topk_select_split(keys, nb, k, blocks, workspace=ws, stream=stream)
         topk.sort_candidate_blocks(blocks, ln, ptab, ps, out_pages=pages, n_cols=w.n_cols, stream=stream)
 
     chain()
     res["amax8_1024x131072"] = rate(amax_bytes, time_us(step_amax, stream))
     res["topk_select_block_keys_1024x16384_k512"] = rate(sel_bytes, time_us(step_select, stream))
+    res["topk_select_split_block_keys_1024x16384_k512"] = rate(sel_bytes, time_us(step_select_split, stream))
     copy_us = time_us(lambda: blocks.copy_(sel), stream)
     table_us = time_us(step_table, stream) - copy_us
     res["block_table_1024_k512"] = rate(tab_bytes, table_us)

@@ -1,6 +1,6 @@
 // Exact per-row top-k over long, ragged fp32 rows, for gfx950 (CDNA4).
 //
-// One persistent launch: one 16-wave workgroup per compute unit, each with
+// One persistent launch: one 12-wave workgroup per compute unit, each with
 // two LDS survivor buffers. A workgroup's rows are dealt to it in a fixed
 // order (longest first over the whole batch, dealt out in a snake, so every
 // workgroup gets about the same number of scores) and flow through three
@@ -10,7 +10,7 @@
 //  * wave 1 claims rows and estimates each one's cutoff key T from a sample
 //    of the row (vLLM PR #56346 report, summary and implementation item 1: a
 //    sampled cutoff, then exact selection among the survivors);
-//  * waves 2-15 read each row once, in chunks handed out one at a time, with
+//  * waves 2-11 read each row once, in chunks handed out one at a time, with
 //    16-byte buffer loads kept in flight across row boundaries, and append
 //    every score with key >= T to the row's buffer with one LDS atomic per
 //    wave and 4 loads, counting on past the capacity without writing (vLLM
@@ -47,7 +47,7 @@ namespace {
 #define TOPK_WAVES 12
 #endif
 constexpr int kThreads = 64 * TOPK_WAVES;                  // finisher, sampler, streamers
-constexpr int kFirstStreamer = 2;                          // waves 2..15 stream
+constexpr int kFirstStreamer = 2;                          // waves 2..11 stream
 constexpr int kCapacity = 7168;                            // survivor entries per buffer
 #ifndef TOPK_UNROLL
 #define TOPK_UNROLL 8

@@ -156,9 +156,13 @@ __device__ uint32_t split_cutoff(const SplitParams& p, int64_t b, int64_t L, uin
     const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
     if (wantf >= (float)n) return 0u;
     const uint32_t want = (uint32_t)wantf;
-    // exact, or the lower edge of a bin whose keys are exactly the top `want`:
-    // either way at most the want-th largest sample key
-    return radix_select<B>(lds, LdsKeys{skey, n}, KeyView{}, want, 0u, 32, n).value;
+    // two 11-bit digits: the want-th largest sample key's top 22 bits (or a
+    // lower edge at which exactly `want` keys start); T is that prefix's
+    // lowest key, so at most the want-th largest sample key, and at most
+    // 2^10 keys (1/8192 of a binade) below it
+    constexpr int kDropBits = 32 - 2 * kDigitBits;
+    return radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, want, 0u, 2 * kDigitBits, n).value
+           << kDropBits;
 }
 
 __global__ __launch_bounds__(kThreads) void split_sample_kernel(SplitParams p) {
@@ -207,6 +211,39 @@ __device__ __forceinline__ uint32_t wave_reserve_n(uint32_t* counter, uint32_t c
     return base + incl - cnt;
 }
 
+__device__ __forceinline__ void load_round(const f4* r4, int64_t base, int64_t g1, f4 (&x)[kUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t g = base + u * kThreads + threadIdx.x;
+        x[u] = g < g1 ? load_nt(r4 + g) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
+__device__ __forceinline__ void filter_round(const f4 (&x)[kUnroll], int64_t base, int64_t g1, uint32_t T, SplitHead* h,
+                                             uint2* surv, uint32_t cap) {
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const bool in = base + u * kThreads + threadIdx.x < g1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt += (in && order_key(x[u][j]) >= T) ? 1u : 0u;
+    }
+    uint32_t slot = wave_reserve_n(&h->count, cnt);
+    if (cnt != 0u) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t g = base + u * kThreads + threadIdx.x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (g < g1 && order_key(x[u][j]) >= T) {
+                    if (slot < cap) surv[slot] = make_uint2(__float_as_uint(x[u][j]), (uint32_t)(4 * g + j));
+                    ++slot;
+                }
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ void stream_piece(const SplitParams& p, int64_t b, int64_t L, uint32_t T, int piece,
                                              SplitHead* h, uint2* surv, uint32_t cap) {
     const int64_t nvec = L >> 2;
@@ -214,34 +251,19 @@ __device__ __forceinline__ void stream_piece(const SplitParams& p, int64_t b, in
     const int64_t g1 = g0 + p.piece_vec < nvec ? g0 + p.piece_vec : nvec;
     const float* row = p.scores + b * p.row_stride;
     const f4* r4 = reinterpret_cast<const f4*>(row);
-    for (int64_t base = g0; base < g1; base += kRound) {  // uniform over the workgroup
-        f4 x[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t g = base + u * kThreads + threadIdx.x;
-            x[u] = g < g1 ? load_nt(r4 + g) : f4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-        uint32_t cnt = 0u;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const bool in = base + u * kThreads + threadIdx.x < g1;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) cnt += (in && order_key(x[u][j]) >= T) ? 1u : 0u;
-        }
-        uint32_t slot = wave_reserve_n(&h->count, cnt);
-        if (cnt != 0u) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t g = base + u * kThreads + threadIdx.x;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (g < g1 && order_key(x[u][j]) >= T) {
-                        if (slot < cap) surv[slot] = make_uint2(__float_as_uint(x[u][j]), (uint32_t)(4 * g + j));
-                        ++slot;
-                    }
-                }
-            }
-        }
+    // two rounds in flight: the next round's loads are issued before this
+    // round is filtered (loops uniform over the workgroup)
+    f4 a[kUnroll], c[kUnroll];
+    int64_t base = g0;
+    if (base < g1) load_round(r4, base, g1, a);
+    while (base < g1) {
+        if (base + kRound < g1) load_round(r4, base + kRound, g1, c);
+        filter_round(a, base, g1, T, h, surv, cap);
+        base += kRound;
+        if (base >= g1) break;
+        if (base + kRound < g1) load_round(r4, base + kRound, g1, a);
+        filter_round(c, base, g1, T, h, surv, cap);
+        base += kRound;
     }
     // the L % 4 scores past the last full group belong to the piece holding
     // that group's successor; its first wave appends them

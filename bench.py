@@ -338,9 +338,9 @@ def indexer_kernels(topk, wls, d_scores, d_len, stream):
     launches: bf16 top-k over 1024 x 16384 consumer rows (k=2048, paged,
     page_size 64), and the two-level indexer over the 128K decode batch
     (block max with topk=512 -> fp32 top-k of 512 blocks over the block keys
-    -> block table, page_size 64), each step and the chain. The block keys are
-    selected both ways, one workgroup per row and split; the chain uses the
-    split entry."""
+    -> block table, page_size 64), each step and the chain. The block keys
+    (short rows) are selected both by topk_select and by the split-row entry;
+    the chain uses topk_select."""
     import torch
 
     import synth
@@ -398,9 +398,8 @@ def indexer_kernels(topk, wls, d_scores, d_len, stream):
         topk.sort_candidate_blocks(blocks, ln, ptab, ps, out_pages=pages, n_cols=w.n_cols, stream=stream)
 
     def chain():
-        # short rows (16384 block keys): the split-row entry selects them faster
         step_amax()
-        topk.topk_select_split(keys, nb, k, blocks, workspace=ws, stream=stream)
+        topk.topk_select(keys, nb, k, blocks, stream=stream)
         topk.sort_candidate_blocks(blocks, ln, ptab, ps, out_pages=pages, n_cols=w.n_cols, stream=stream)
 
     chain()

@@ -1,0 +1,25 @@
+// The short-row selection kernel's launcher, shared between translation units
+// of the library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace topk {
+
+// Widest rows the short-row kernel takes: the automatic path of topk_select
+// routes batches whose n_cols is at most this to it.
+#ifndef TOPK_SHORT_MAX_COLS
+#define TOPK_SHORT_MAX_COLS 32768
+#endif
+constexpr int64_t kShortMaxCols = TOPK_SHORT_MAX_COLS;
+
+// One workgroup per row: sample, one streaming pass into an LDS survivor
+// buffer, exact selection there (full-row selection on overflow or
+// underflow). Arguments as for topk_select; the caller has checked them.
+// Returns a TOPK_* status.
+int launch_short_rows(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                      const int32_t* lengths, int32_t k, int32_t* out_idx, const int32_t* page_table,
+                      int64_t page_table_stride, int32_t page_size, int32_t* row_stats, hipStream_t stream);
+
+}  // namespace topk

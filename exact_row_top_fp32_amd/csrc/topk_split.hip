@@ -37,6 +37,7 @@
 
 #include "exact_topk.h"
 #include "topk_device.h"
+#include "topk_short.h"
 
 namespace topk {
 namespace {
@@ -337,6 +338,109 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
     if (threadIdx.x == 0) split_stats(p, b, code, head.kind == kKindFull ? (uint32_t)L : n);
 }
 
+// ----------------------------------------------------------------------------
+// short rows: one workgroup per row, survivors in LDS, one launch
+// ----------------------------------------------------------------------------
+
+// Survivor entries a short-row workgroup holds in LDS. Rows of at most
+// kShortMaxCols scores with k <= 2048 keep about 2900 survivors at most on
+// average (the sample's rank rule), so overflow needs a row far from its
+// sample's picture; it then takes the full-row selection.
+constexpr int kShortCap = 3840;
+
+__global__ __launch_bounds__(kThreads) void short_rows_kernel(SplitParams p) {
+    using B = BlockScope<kThreads>;
+    __shared__ uint2 buf[kShortCap];  // the sample's keys first, then the survivors
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t found[3];
+    __shared__ uint32_t count;
+    __shared__ uint32_t emitted;
+    static_assert(kShortCap * 2 >= kMaxSample, "the sample fits the survivor buffer");
+    const int64_t b = blockIdx.x;
+    const int64_t L = split_row_len(p, b);
+    const uint32_t m = (uint32_t)(L < p.k ? L : p.k);
+    if (L <= p.k) {
+        const OutRow out = split_out_row(p, b, m, nullptr);
+        for (int64_t i = threadIdx.x; i < p.k; i += kThreads) out.row[i] = i < L ? out.map((uint32_t)i) : -1;
+        if (threadIdx.x == 0) split_stats(p, b, L == 0 ? TOPK_ROW_EMPTY : TOPK_ROW_ALL, (uint32_t)L);
+        return;
+    }
+    for (int i = (int)threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
+    if (threadIdx.x == 0) {
+        count = 0u;
+        emitted = 0u;
+    }
+    B::sync();
+    const SelectLds lds{hist, found};
+    const bool keep_all = L <= kShortCap;
+    const uint32_t T = keep_all ? 0u : split_cutoff(p, b, L, m, reinterpret_cast<uint32_t*>(buf), lds);
+    B::sync();  // the sample's keys are read; the buffer takes survivors now
+
+    // one streaming pass, two rounds of loads in flight; hits go to LDS
+    const int64_t nvec = L >> 2;
+    const float* row = p.scores + b * p.row_stride;
+    const f4* r4 = reinterpret_cast<const f4*>(row);
+    auto filter = [&](const f4 (&x)[kUnroll], int64_t base) {
+        uint32_t cnt = 0u;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const bool in = base + u * kThreads + threadIdx.x < nvec;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cnt += (in && order_key(x[u][j]) >= T) ? 1u : 0u;
+        }
+        uint32_t slot = wave_reserve_n(&count, cnt);
+        if (cnt != 0u) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t g = base + u * kThreads + threadIdx.x;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (g < nvec && order_key(x[u][j]) >= T) {
+                        if (slot < (uint32_t)kShortCap)
+                            buf[slot] = make_uint2(__float_as_uint(x[u][j]), (uint32_t)(4 * g + j));
+                        ++slot;
+                    }
+                }
+            }
+        }
+    };
+    f4 xa[kUnroll], xc[kUnroll];
+    int64_t base = 0;
+    if (base < nvec) load_round(r4, base, nvec, xa);
+    while (base < nvec) {  // uniform over the workgroup
+        if (base + kRound < nvec) load_round(r4, base + kRound, nvec, xc);
+        filter(xa, base);
+        base += kRound;
+        if (base >= nvec) break;
+        if (base + kRound < nvec) load_round(r4, base + kRound, nvec, xa);
+        filter(xc, base);
+        base += kRound;
+    }
+    if (nvec * 4 < L && threadIdx.x < 64) {  // the L % 4 scores past the last group
+        const int64_t i = nvec * 4 + threadIdx.x;
+        const float v = i < L ? row[i] : 0.0f;
+        const bool hit = i < L && order_key(v) >= T;
+        const uint32_t slot = wave_reserve_n(&count, hit ? 1u : 0u);
+        if (hit && slot < (uint32_t)kShortCap) buf[slot] = make_uint2(__float_as_uint(v), (uint32_t)i);
+    }
+    B::sync();
+    const uint32_t n = count;
+    OutRow out = split_out_row(p, b, m, &emitted);
+    int code;
+    if (n > (uint32_t)kShortCap || n < m) {
+        code = n > (uint32_t)kShortCap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
+        const RowSource<B> src{row, L};
+        const Selection s = select_top<B>(lds, src, m, (uint32_t)L, 0u, 0xFFFFFFFFu, bits_for(L));
+        emit(src, s, out);
+    } else {
+        code = keep_all ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
+        const PairSource<B> src{buf, n};
+        const Selection s = select_top<B>(lds, src, m, n, T, 0xFFFFFFFFu, bits_for(L));
+        emit(src, s, out);
+    }
+    if (threadIdx.x == 0) split_stats(p, b, code, n);
+}
+
 int split_device_cus() {
     static std::atomic<int> cached[64];
     int dev = 0;
@@ -352,6 +456,19 @@ int split_device_cus() {
 }
 
 }  // namespace
+
+int launch_short_rows(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                      const int32_t* lengths, int32_t k, int32_t* out_idx, const int32_t* page_table,
+                      int64_t page_table_stride, int32_t page_size, int32_t* row_stats, hipStream_t stream) {
+    if (batch * kThreads > (int64_t)UINT32_MAX) return TOPK_ERR_ARG;
+    SplitParams p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride, page_size, k,
+                  TOPK_PATH_AUTO, kShortCap, row_stats, batch, nullptr, nullptr, 0, 1};
+    void* args[] = {&p};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&short_rows_kernel), dim3((uint32_t)batch),
+                                         dim3(kThreads), args, 0, stream);
+    return e == hipSuccess ? TOPK_OK : TOPK_ERR_LAUNCH;
+}
+
 }  // namespace topk
 
 using namespace topk;

@@ -375,3 +375,47 @@ def test_rows_sharing_a_length_bucket(topk, layout):
         bad = check_fast_raw(got, want, wl.lengths, wl.n_cols, wl.k)
         assert not bad, f"rows differing from the oracle: {bad[:10]}"
     assert_parity(wl, got, want)
+
+
+# ----------------------------------------------------------------------------
+# short rows on the automatic path (n_cols <= 32768): one workgroup per row
+# ----------------------------------------------------------------------------
+
+SHORT_MAX_COLS = 32768
+SHORT_CAP = 3840  # survivors the short-row kernel holds in LDS
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_short_rows_buffer_boundaries(topk, k):
+    W = 20000
+    lens = [SHORT_CAP - 1, SHORT_CAP, SHORT_CAP + 1, SHORT_CAP + 3, k + 1, 2 * SHORT_CAP, W - 3, W]
+    wl = synth.mixed_rows(["normal", "heavy_ties", "ascending", "signed_zero"] * 2, W, k, seed=35)
+    wl.lengths = np.array(lens, np.int32)
+    synth.poison_tails(wl.scores, wl.lengths)
+    got, stats = run(topk, wl, want_stats=True)
+    assert_parity(wl, got, expect(wl))
+    codes = stats[:, 0].tolist()
+    assert codes[0] == 2 and codes[1] == 2, "rows up to the buffer keep every score"
+    assert all(c in (3, 4, 5) for c in codes[2:4]) and codes[4] == (2 if k + 1 <= SHORT_CAP else 3)
+
+
+@pytest.mark.parametrize("W", [SHORT_MAX_COLS, SHORT_MAX_COLS + 4])
+def test_short_row_threshold_widths(topk, W):
+    # the widest batch the short-row kernel takes, and one the persistent
+    # kernel takes, both exact
+    wl = synth.mixed_rows(["normal", "crowd4096", "onebin", "clustered_peaks"] * 2, W, 2048, seed=36)
+    wl.lengths = np.array([W, W - 1, W - 2, W - 3, 5000, 4097, 2049, 1], np.int32)
+    synth.poison_tails(wl.scores, wl.lengths)
+    got, _ = run(topk, wl)
+    assert_parity(wl, got, expect(wl))
+
+
+def test_short_rows_overflow_fallback(topk):
+    # rows whose sample hides a crowd just above the cutoff: more survivors
+    # than the LDS buffer holds, so the full-row selection runs
+    wl = synth.c2(2048)
+    got, stats = run(topk, wl, want_stats=True)
+    assert_parity(wl, got, expect(wl))
+    paths = dict(zip(*np.unique(stats[:, 0], return_counts=True)))
+    say("  short-row paths on the adversarial rows:", paths)
+    assert paths.get(4, 0) > 0, "some adversarial row overflows the buffer"

@@ -33,9 +33,11 @@
  * position, and writes only out_idx[0:batch, 0:k) (and row_stats).
  *
  * Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the default
- * stream) and never synchronise. Each call is one launch on that stream: a
- * persistent kernel with one workgroup per compute unit, whose LDS (about
- * 157 KB) leaves room for no other workgroup on the unit while it runs.
+ * stream) and never synchronise. Each call of topk_select is one launch on
+ * that stream: for n_cols <= 32768 (and no forced path or capacity), one
+ * workgroup per row with the row's survivors in LDS; otherwise a persistent
+ * kernel with one workgroup per compute unit, whose LDS (about 157 KB) leaves
+ * room for no other workgroup on the unit while it runs.
  * Argument errors are returned synchronously
  * as a status code before anything is launched; device data (lengths, page
  * table contents) is never an error: lengths are clamped to [0, n_cols].

@@ -2,12 +2,9 @@
 // indexer, for gfx950 ("dsv4.1: Top-k kernels and candidate selection",
 // implementation section 2 and code excerpts):
 //
-//  * topk_bf16_kernel: exact top-k of bf16 rows of at most 16384 scores, one
-//    workgroup per row with the row in registers: a histogram of the 16-bit
-//    order keys' top 11 bits locates the bin of the k-th largest; only that
-//    bin's elements go to LDS, as unique values (low key bits, then inverted
-//    position), and a radix select among them ends the selection with the
-//    lowest positions first among equal scores;
+//  * bf16 top-k (topk_select_bf16): rows of at most 16384 scores, each
+//    widened exactly to fp32 as it is loaded, selected by the short-row
+//    kernel (one workgroup per row, sampled cutoff, survivors in LDS);
 //  * amax8_kernel: the level-one keys, the largest of every 8 scores (NaN
 //    ignored, +0 above -0) with the newest block +inf; a streaming kernel in
 //    which two lanes read the two halves of a block, so that every wave load
@@ -20,167 +17,12 @@
 
 #include "exact_topk.h"
 #include "topk_device.h"
+#include "topk_short.h"
 
 namespace topk {
 namespace {
 
-// ----------------------------------------------------------------------------
-// bf16 rows
-// ----------------------------------------------------------------------------
-
-constexpr int kBfThreads = 512;
-constexpr int kBfMaxCols = 16384;
-constexpr int kBfChunks = kBfMaxCols / 8 / kBfThreads;  // 16-byte chunks per lane
-constexpr int kBfShift = 5;                              // first digit: key bits 15..5
-
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-
-struct Bf16Params {
-    const uint16_t* scores;
-    int64_t row_stride;
-    int64_t n_cols;
-    const int32_t* lengths;
-    int32_t* out;
-    const int32_t* page_table;
-    int64_t pt_stride;
-    int32_t page_size;
-    int32_t page_shift;  // log2(page_size) when it is a power of two, else -1
-    int32_t k;
-};
-
-// bf16 pattern -> 16-bit key in value order (negative patterns inverted,
-// non-negative ones get the top bit): -0 just below +0, -inf lowest.
-__device__ __forceinline__ uint32_t bf16_key(uint32_t h) {
-    return (h ^ ((0u - (h >> 15)) | 0x8000u)) & 0xFFFFu;
-}
-
-// Within one first-digit bin, an element's rank value: its low key bits above
-// its inverted position. Unique per element, larger = better (higher key,
-// then lower position), so the need-th largest of them ends the selection.
-__device__ __forceinline__ uint32_t bf16_packed(uint32_t key, uint32_t idx) {
-    return ((key & ((1u << kBfShift) - 1u)) << 16) | (0xFFFFu - idx);
-}
-
-// Candidates (packed rank values) in LDS.
-struct Bf16Cands {
-    const uint32_t* v;
-    uint32_t n;
-    template <class F>
-    __device__ __forceinline__ void for_each(F&& f) const {
-        for (uint32_t e = threadIdx.x; e < n; e += kBfThreads) f(v[e], e);
-    }
-};
-
-// Lane t's chunk c holds positions (c * 512 + t) * 8 .. + 7; f(key, idx) for
-// each of them below L. Uniform over the workgroup (no early exit).
-template <class F>
-__device__ __forceinline__ void bf16_each(const u4 (&v)[kBfChunks], uint32_t L, F&& f) {
-#pragma unroll
-    for (int c = 0; c < kBfChunks; ++c) {
-        const uint32_t base = (uint32_t)(c * kBfThreads + threadIdx.x) * 8u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t idx = base + (uint32_t)e;
-            f(bf16_key((v[c][e >> 1] >> (16 * (e & 1))) & 0xFFFFu), idx, idx < L);
-        }
-    }
-}
-
-// Every lane's `cnt` slots from an LDS counter, one atomic per wave; all
-// lanes of the wave active.
-__device__ __forceinline__ uint32_t wave_slots(uint32_t* counter, uint32_t cnt) {
-    const uint32_t incl = wave_inclusive_sum(cnt);
-    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
-    uint32_t base = 0u;
-    if (total != 0u) {
-        if (lane_id() == 0) base = atomicAdd(counter, total);
-        base = __builtin_amdgcn_readfirstlane(base);
-    }
-    return base + incl - cnt;
-}
-
-__global__ __launch_bounds__(kBfThreads, 4) void topk_bf16_kernel(Bf16Params p) {
-    using B = BlockScope<kBfThreads>;
-    __shared__ uint32_t cand[kBfMaxCols];
-    __shared__ uint32_t hist[kBins];
-    __shared__ uint32_t found[3];
-    __shared__ uint32_t ncand;
-    __shared__ uint32_t emitted;
-    const int64_t b = blockIdx.x;
-    int64_t Lr = p.lengths ? (int64_t)p.lengths[b] : p.n_cols;
-    Lr = Lr < 0 ? 0 : (Lr > p.n_cols ? p.n_cols : Lr);
-    const uint32_t L = (uint32_t)Lr;
-    const uint32_t m = L < (uint32_t)p.k ? L : (uint32_t)p.k;
-    int32_t* orow = p.out + b * (int64_t)p.k;
-    const int32_t* pages = p.page_table ? p.page_table + b * p.pt_stride : nullptr;
-    auto map = [&](uint32_t i) -> int32_t {
-        if (pages == nullptr) return (int32_t)i;
-        const uint32_t ps = (uint32_t)p.page_size;
-        const uint32_t pg = p.page_shift >= 0 ? i >> p.page_shift : i / ps;
-        const uint32_t off = p.page_shift >= 0 ? i & (ps - 1u) : i % ps;
-        return (int32_t)((int64_t)pages[pg] * (int64_t)ps + (int64_t)off);
-    };
-    if (L <= (uint32_t)p.k) {  // every position, then -1
-        for (int i = (int)threadIdx.x; i < p.k; i += kBfThreads) orow[i] = (uint32_t)i < L ? map((uint32_t)i) : -1;
-        return;
-    }
-    // all loads in flight before any use
-    const uint16_t* row = p.scores + b * p.row_stride;
-    u4 v[kBfChunks];
-#pragma unroll
-    for (int c = 0; c < kBfChunks; ++c) {
-        const uint32_t base = (uint32_t)(c * kBfThreads + threadIdx.x) * 8u;
-        if (base + 8u <= L) {
-            v[c] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(row + base));
-        } else {
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
-            for (uint32_t e = 0; e < 8u && base + e < L; ++e) w[e >> 1] |= (uint32_t)row[base + e] << (16 * (e & 1));
-            v[c] = u4{w[0], w[1], w[2], w[3]};
-        }
-    }
-    for (int i = (int)threadIdx.x; i < kBins; i += kBfThreads) hist[i] = 0u;
-    if (threadIdx.x == 0) {
-        ncand = 0u;
-        emitted = 0u;
-    }
-    B::sync();
-    // the bin of the m-th largest key's top 11 bits
-    bf16_each(v, L, [&](uint32_t key, uint32_t, bool live) {
-        if (live) atomicAdd(&hist[key >> kBfShift], 1u);
-    });
-    B::sync();
-    const Found f = find_rank_bin<B>(SelectLds{hist, found}, m);
-    const uint32_t need = m - f.above;  // taken from bin f.digit, 1 <= need <= f.count
-    uint32_t cut = 0u;                  // take packed values >= cut within the bin
-    if (need < f.count) {
-        // that bin's elements as packed rank values, then the need-th largest
-        uint32_t cnt = 0u;
-        bf16_each(v, L, [&](uint32_t key, uint32_t, bool live) { cnt += (live && (key >> kBfShift) == f.digit) ? 1u : 0u; });
-        uint32_t slot = wave_slots(&ncand, cnt);
-        bf16_each(v, L, [&](uint32_t key, uint32_t idx, bool live) {
-            if (live && (key >> kBfShift) == f.digit) cand[slot++] = bf16_packed(key, idx);
-        });
-        B::sync();
-        // unique values: exact, or a lower edge with exactly `need` at or above it
-        cut = radix_select<B>(SelectLds{hist, found}, Bf16Cands{cand, f.count}, KeyView{}, need, 0u,
-                              kBfShift + 16, f.count).value;
-    }
-    // emission: lanes count what they take, one reservation per wave, then
-    // write their positions to consecutive slots
-    auto take = [&](uint32_t key, uint32_t idx, bool live) {
-        const uint32_t d = key >> kBfShift;
-        return live && (d > f.digit || (d == f.digit && bf16_packed(key, idx) >= cut));
-    };
-    uint32_t cnt = 0u;
-    bf16_each(v, L, [&](uint32_t key, uint32_t idx, bool live) { cnt += take(key, idx, live) ? 1u : 0u; });
-    uint32_t slot = wave_slots(&emitted, cnt);
-    bf16_each(v, L, [&](uint32_t key, uint32_t idx, bool live) {
-        if (take(key, idx, live)) {
-            if (slot < m) orow[slot] = map(idx);
-            ++slot;
-        }
-    });
-}
+constexpr int kBfMaxCols = 16384;  // bf16 rows: at most this many scores
 
 // ----------------------------------------------------------------------------
 // block max of every 8 scores
@@ -338,7 +180,7 @@ int topk_select_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, 
                      const int32_t* lengths, int32_t k, int32_t* out_idx,
                      const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
                      void* hip_stream) {
-    if (batch < 0 || batch > (int64_t)(UINT32_MAX / kBfThreads)) return TOPK_ERR_ARG;
+    if (batch < 0 || batch > (int64_t)(UINT32_MAX / 256)) return TOPK_ERR_ARG;
     if (k < 1 || k > TOPK_MAX_K) return TOPK_ERR_K;
     if (n_cols < 0 || n_cols > kBfMaxCols || row_stride < n_cols) return TOPK_ERR_ARG;
     if (page_table != nullptr) {
@@ -349,12 +191,8 @@ int topk_select_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, 
     if (scores == nullptr || out_idx == nullptr) return TOPK_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(scores) & 15u) != 0) return TOPK_ERR_ALIGN;
     if (batch > 1 && (row_stride & 7) != 0) return TOPK_ERR_ALIGN;
-    const int32_t shift = (page_table != nullptr && (page_size & (page_size - 1)) == 0) ? __builtin_ctz((unsigned)page_size) : -1;
-    Bf16Params p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride, page_size, shift, k};
-    void* args[] = {&p};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&topk_bf16_kernel), dim3((uint32_t)batch),
-                                         dim3(kBfThreads), args, 0, static_cast<hipStream_t>(hip_stream));
-    return e == hipSuccess ? TOPK_OK : TOPK_ERR_LAUNCH;
+    return launch_short_rows_bf16(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
+                                  page_table_stride, page_size, static_cast<hipStream_t>(hip_stream));
 }
 
 int amax8_varlen(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols, const int32_t* lengths,

@@ -1,4 +1,4 @@
-// The short-row selection kernel's launcher, shared between translation units
+// The short-row selection kernel's launchers, shared between translation units
 // of the library (not part of the C ABI).
 #pragma once
 
@@ -21,5 +21,12 @@ constexpr int64_t kShortMaxCols = TOPK_SHORT_MAX_COLS;
 int launch_short_rows(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
                       const int32_t* lengths, int32_t k, int32_t* out_idx, const int32_t* page_table,
                       int64_t page_table_stride, int32_t page_size, int32_t* row_stats, hipStream_t stream);
+
+// The same kernel over bf16 rows (bit patterns, 16-byte aligned rows with
+// row_stride % 8 == 0): each score widened exactly to fp32, so the selection
+// is the fp32 one on the widened row.
+int launch_short_rows_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                           const int32_t* lengths, int32_t k, int32_t* out_idx, const int32_t* page_table,
+                           int64_t page_table_stride, int32_t page_size, hipStream_t stream);
 
 }  // namespace topk

@@ -26,9 +26,17 @@
 //     candidate bins overflow", comment thread: cutoff first).
 //
 // Kernel boundaries order the three steps, so no workgroup waits for another
-// and no device-scope fence is needed. The selected set is the one every
-// other path returns: all positions whose key is above the cutoff key, then
-// the lowest positions equal to it.
+// and no device-scope fence is needed.
+//
+// The same pieces serve short rows in a single launch (short_rows_kernel):
+// one workgroup per row takes the sample, streams the row once into an LDS
+// survivor buffer and selects there, falling back to the full-row selection
+// when the buffer overflows or the survivors fall short of m. topk_select
+// sends rows of at most 32768 scores here; topk_select_bf16 sends every bf16
+// row, widening each score exactly to fp32 as it is loaded.
+//
+// The selected set is the one every other path returns: all positions whose
+// key is above the cutoff key, then the lowest positions equal to it.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -348,8 +356,103 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
 // sample's picture; it then takes the full-row selection.
 constexpr int kShortCap = 3840;
 
-__global__ __launch_bounds__(kThreads) void short_rows_kernel(SplitParams p) {
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// Element types of a score row, read 16 bytes at a time: fp32, or bf16 (its
+// bit pattern, the top half of the fp32 it denotes exactly). bits() gives the
+// fp32 pattern of element j of a load, so keys, survivors and selection are
+// the fp32 ones for both.
+struct F32Elem {
+    typedef f4 Vec;
+    typedef float Scalar;
+    static constexpr int kPerVec = 4;
+    static constexpr int kUnroll = 8;  // loads per lane per round: 32 scores
+    __device__ static uint32_t bits(const Vec& v, int j) { return __float_as_uint(v[j]); }
+    __device__ static uint32_t scalar_bits(Scalar x) { return __float_as_uint(x); }
+};
+struct Bf16Elem {
+    typedef u4 Vec;
+    typedef uint16_t Scalar;
+    static constexpr int kPerVec = 8;
+    static constexpr int kUnroll = 4;  // loads per lane per round: 32 scores
+    __device__ static uint32_t bits(const Vec& v, int j) {
+        return (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
+    }
+    __device__ static uint32_t scalar_bits(Scalar x) { return (uint32_t)x << 16; }
+};
+
+template <class E>
+__device__ __forceinline__ uint32_t elem_key(uint32_t bits) { return order_key(__uint_as_float(bits)); }
+
+// Every score of a row in global memory (the full-row selection's source).
+template <class S, class E>
+struct ElemRowSource {
+    const typename E::Scalar* row;
+    int64_t len;
+    template <class F>
+    __device__ void for_each(F&& f) const {
+        const typename E::Vec* rv = reinterpret_cast<const typename E::Vec*>(row);
+        const int64_t nvec = len / E::kPerVec;
+        for (int64_t v = S::rank(); v < nvec; v += S::kSize) {
+            const typename E::Vec x = rv[v];
+#pragma unroll
+            for (int j = 0; j < E::kPerVec; ++j)
+                f(elem_key<E>(E::bits(x, j)), (uint32_t)(E::kPerVec * v + j));
+        }
+        for (int64_t i = E::kPerVec * nvec + S::rank(); i < len; i += S::kSize)
+            f(elem_key<E>(E::scalar_bits(row[i])), (uint32_t)i);
+    }
+};
+
+// The cutoff key of a short row from its sample: `runs` runs of 64 scores at
+// evenly spaced offsets, the same rank rule as the split-row mode, two 11-bit
+// digits (T at most 2^10 keys below the wanted sample key).
+template <class E>
+__device__ uint32_t short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, uint32_t* skey,
+                                 SelectLds lds) {
     using B = BlockScope<kThreads>;
+    const int64_t fit = L / (2 * kRunLen);
+    const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
+    if (runs < 2) return 0u;
+    constexpr int kVecPerRun = kRunLen / E::kPerVec;
+    constexpr int kPer = kMaxSample / E::kPerVec / kThreads;  // loads per lane, all in flight
+    const int nsv = runs * kVecPerRun;
+    const int64_t span = L - kRunLen;
+    const typename E::Vec* rv = reinterpret_cast<const typename E::Vec*>(row);
+    typename E::Vec x[kPer];
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+        const int t = h * kThreads + (int)threadIdx.x;
+        const int r = t / kVecPerRun;
+        // run r starts at floor(r * span / (runs - 1)), rounded down to a load
+        const int64_t start = ((int64_t)r * span / (runs - 1)) / E::kPerVec;
+        if (t < nsv) x[h] = rv[start + t % kVecPerRun];
+    }
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+        const int t = h * kThreads + (int)threadIdx.x;
+        if (t < nsv) {
+#pragma unroll
+            for (int j = 0; j < E::kPerVec; ++j) skey[E::kPerVec * t + j] = elem_key<E>(E::bits(x[h], j));
+        }
+    }
+    B::sync();
+    const uint32_t n = (uint32_t)(E::kPerVec * nsv);
+    const float mu = (float)m * (float)n / (float)L;
+    const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
+    if (wantf >= (float)n) return 0u;
+    constexpr int kDropBits = 32 - 2 * kDigitBits;
+    return radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, (uint32_t)wantf, 0u, 2 * kDigitBits, n)
+               .value
+           << kDropBits;
+}
+
+template <class E>
+__global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) {
+    constexpr int kU = E::kUnroll;
+    constexpr int64_t kR = (int64_t)kThreads * kU;  // loads per workgroup round
+    using B = BlockScope<kThreads>;
+    typedef typename E::Vec Vec;
     __shared__ uint2 buf[kShortCap];  // the sample's keys first, then the survivors
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t found[3];
@@ -372,56 +475,63 @@ __global__ __launch_bounds__(kThreads) void short_rows_kernel(SplitParams p) {
     }
     B::sync();
     const SelectLds lds{hist, found};
+    const typename E::Scalar* row = reinterpret_cast<const typename E::Scalar*>(p.scores) + b * p.row_stride;
     const bool keep_all = L <= kShortCap;
-    const uint32_t T = keep_all ? 0u : split_cutoff(p, b, L, m, reinterpret_cast<uint32_t*>(buf), lds);
+    const uint32_t T = keep_all ? 0u : short_cutoff<E>(row, L, m, reinterpret_cast<uint32_t*>(buf), lds);
     B::sync();  // the sample's keys are read; the buffer takes survivors now
 
     // one streaming pass, two rounds of loads in flight; hits go to LDS
-    const int64_t nvec = L >> 2;
-    const float* row = p.scores + b * p.row_stride;
-    const f4* r4 = reinterpret_cast<const f4*>(row);
-    auto filter = [&](const f4 (&x)[kUnroll], int64_t base) {
+    const int64_t nvec = L / E::kPerVec;
+    const Vec* rv = reinterpret_cast<const Vec*>(row);
+    auto load = [&](int64_t base, Vec (&x)[kU]) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t g = base + u * kThreads + threadIdx.x;
+            if (g < nvec) x[u] = __builtin_nontemporal_load(rv + g);
+        }
+    };
+    auto filter = [&](const Vec (&x)[kU], int64_t base) {
         uint32_t cnt = 0u;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kU; ++u) {
             const bool in = base + u * kThreads + threadIdx.x < nvec;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cnt += (in && order_key(x[u][j]) >= T) ? 1u : 0u;
+            for (int j = 0; j < E::kPerVec; ++j) cnt += (in && elem_key<E>(E::bits(x[u], j)) >= T) ? 1u : 0u;
         }
         uint32_t slot = wave_reserve_n(&count, cnt);
         if (cnt != 0u) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < kU; ++u) {
                 const int64_t g = base + u * kThreads + threadIdx.x;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (g < nvec && order_key(x[u][j]) >= T) {
-                        if (slot < (uint32_t)kShortCap)
-                            buf[slot] = make_uint2(__float_as_uint(x[u][j]), (uint32_t)(4 * g + j));
+                for (int j = 0; j < E::kPerVec; ++j) {
+                    const uint32_t bits = E::bits(x[u], j);
+                    if (g < nvec && elem_key<E>(bits) >= T) {
+                        if (slot < (uint32_t)kShortCap) buf[slot] = make_uint2(bits, (uint32_t)(E::kPerVec * g + j));
                         ++slot;
                     }
                 }
             }
         }
     };
-    f4 xa[kUnroll], xc[kUnroll];
+    Vec xa[kU], xc[kU];
     int64_t base = 0;
-    if (base < nvec) load_round(r4, base, nvec, xa);
+    if (base < nvec) load(base, xa);
     while (base < nvec) {  // uniform over the workgroup
-        if (base + kRound < nvec) load_round(r4, base + kRound, nvec, xc);
+        if (base + kR < nvec) load(base + kR, xc);
         filter(xa, base);
-        base += kRound;
+        base += kR;
         if (base >= nvec) break;
-        if (base + kRound < nvec) load_round(r4, base + kRound, nvec, xa);
+        if (base + kR < nvec) load(base + kR, xa);
         filter(xc, base);
-        base += kRound;
+        base += kR;
     }
-    if (nvec * 4 < L && threadIdx.x < 64) {  // the L % 4 scores past the last group
-        const int64_t i = nvec * 4 + threadIdx.x;
-        const float v = i < L ? row[i] : 0.0f;
-        const bool hit = i < L && order_key(v) >= T;
+    if (nvec * E::kPerVec < L && threadIdx.x < 64) {  // the scores past the last full load
+        const int64_t i = nvec * E::kPerVec + threadIdx.x;
+        const uint32_t bits = i < L ? E::scalar_bits(row[i]) : 0u;
+        const bool hit = i < L && elem_key<E>(bits) >= T;
         const uint32_t slot = wave_reserve_n(&count, hit ? 1u : 0u);
-        if (hit && slot < (uint32_t)kShortCap) buf[slot] = make_uint2(__float_as_uint(v), (uint32_t)i);
+        if (hit && slot < (uint32_t)kShortCap) buf[slot] = make_uint2(bits, (uint32_t)i);
     }
     B::sync();
     const uint32_t n = count;
@@ -429,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void short_rows_kernel(SplitParams p) {
     int code;
     if (n > (uint32_t)kShortCap || n < m) {
         code = n > (uint32_t)kShortCap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
-        const RowSource<B> src{row, L};
+        const ElemRowSource<B, E> src{row, L};
         const Selection s = select_top<B>(lds, src, m, (uint32_t)L, 0u, 0xFFFFFFFFu, bits_for(L));
         emit(src, s, out);
     } else {
@@ -457,16 +567,31 @@ int split_device_cus() {
 
 }  // namespace
 
+template <class E>
+int launch_short(const void* scores, int64_t batch, int64_t row_stride, int64_t n_cols, const int32_t* lengths,
+                 int32_t k, int32_t* out_idx, const int32_t* page_table, int64_t page_table_stride,
+                 int32_t page_size, int32_t* row_stats, hipStream_t stream) {
+    if (batch * kThreads > (int64_t)UINT32_MAX) return TOPK_ERR_ARG;
+    SplitParams p{static_cast<const float*>(scores), row_stride, n_cols, lengths, out_idx, page_table,
+                  page_table_stride, page_size, k, TOPK_PATH_AUTO, kShortCap, row_stats, batch, nullptr, nullptr, 0, 1};
+    void* args[] = {&p};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&short_rows_kernel<E>), dim3((uint32_t)batch),
+                                         dim3(kThreads), args, 0, stream);
+    return e == hipSuccess ? TOPK_OK : TOPK_ERR_LAUNCH;
+}
+
 int launch_short_rows(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
                       const int32_t* lengths, int32_t k, int32_t* out_idx, const int32_t* page_table,
                       int64_t page_table_stride, int32_t page_size, int32_t* row_stats, hipStream_t stream) {
-    if (batch * kThreads > (int64_t)UINT32_MAX) return TOPK_ERR_ARG;
-    SplitParams p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride, page_size, k,
-                  TOPK_PATH_AUTO, kShortCap, row_stats, batch, nullptr, nullptr, 0, 1};
-    void* args[] = {&p};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&short_rows_kernel), dim3((uint32_t)batch),
-                                         dim3(kThreads), args, 0, stream);
-    return e == hipSuccess ? TOPK_OK : TOPK_ERR_LAUNCH;
+    return launch_short<F32Elem>(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
+                                 page_table_stride, page_size, row_stats, stream);
+}
+
+int launch_short_rows_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                           const int32_t* lengths, int32_t k, int32_t* out_idx, const int32_t* page_table,
+                           int64_t page_table_stride, int32_t page_size, hipStream_t stream) {
+    return launch_short<Bf16Elem>(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
+                                  page_table_stride, page_size, nullptr, stream);
 }
 
 }  // namespace topk

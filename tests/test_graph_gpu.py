@@ -51,7 +51,8 @@ LENGTH_SETS = [
 ]
 
 
-@pytest.mark.parametrize("entry", ["topk_select", "topk_select_ex_small_capacity", "topk_select_split"])
+@pytest.mark.parametrize("entry", ["topk_select", "topk_select_short_rows", "topk_select_ex_small_capacity",
+                                   "topk_select_split"])
 def test_graph_replay_with_new_lengths_and_scores(topk, entry):
     k, W = 512, 60000
     kinds = ["normal", "clustered_peaks", "onebin", "neginf_half", "heavy_ties", "crowd4096",
@@ -64,9 +65,13 @@ def test_graph_replay_with_new_lengths_and_scores(topk, entry):
     out = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(topk.topk_split_workspace_bytes(B), dtype=torch.uint8, device="cuda")
 
+    n_cols = 30000 if entry == "topk_select_short_rows" else W  # rows of at most 32768: the short-row kernel
+
     def call():
         if entry == "topk_select":
             topk.topk_select(s, ln, k, out)
+        elif entry == "topk_select_short_rows":
+            topk.topk_select(s[:, :n_cols], ln, k, out)
         elif entry == "topk_select_ex_small_capacity":
             topk.topk_select_ex(s, ln, k, out, capacity=700)  # every sampled row overflows
         else:
@@ -75,7 +80,7 @@ def test_graph_replay_with_new_lengths_and_scores(topk, entry):
     say(f"  eager {entry}")
     call()
     torch.cuda.synchronize()
-    parity(host, wl.lengths, W, k, out.cpu().numpy(), expect(host, wl.lengths, W, k))
+    parity(host, wl.lengths, n_cols, k, out.cpu().numpy(), expect(host, wl.lengths, n_cols, k))
 
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -105,5 +110,5 @@ def test_graph_replay_with_new_lengths_and_scores(topk, entry):
         say(f"  replay {rep} of {entry}")
         g.replay()
         torch.cuda.synchronize()
-        parity(host, lens, W, k, out.cpu().numpy(), expect(host, lens, W, k))
+        parity(host, lens, n_cols, k, out.cpu().numpy(), expect(host, lens, n_cols, k))
     assert topk.topk_watchdog_trips() == 0

@@ -11,6 +11,13 @@ the timed region. `value` is the algorithmic bytes of one step (4 B per valid
 score read, 4 B per length read, 4 B per output slot written) divided by the
 wall time per step, in GB/s.
 
+Besides the step, the same JSON line carries two sections timed after it,
+neither part of `value`: `small_batch` (the first 40 rows of each batch, one
+workgroup per row against the split-row entry, eager and replayed from a
+HIP graph) and `indexer` (the bf16 top-k and the two-level indexer's block
+max, block-key top-k and block table, each with its algorithmic bytes and
+fraction of peak).
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations

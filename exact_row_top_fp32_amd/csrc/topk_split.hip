@@ -121,58 +121,108 @@ struct LdsKeys {
 };
 
 // ----------------------------------------------------------------------------
-// launch 1: direct rows, cutoffs and headers
+// score rows and their sampled cutoff (both the split-row and short-row kernels)
 // ----------------------------------------------------------------------------
 
-// The want-th largest key of a sample of row b: `runs` runs of 64 contiguous
-// scores at evenly spaced offsets over [0, L). When the sample has fewer
-// than `want` keys above the row's m-th largest, fewer than m scores can be
-// at or above T; the rank is set so that this is a six-sigma event: the
-// number of sample keys at or above the m-th largest score is binomial with
-// mean mu = m n / L, and want = ceil(mu + 6 sqrt(mu) + 4).
-__device__ uint32_t split_cutoff(const SplitParams& p, int64_t b, int64_t L, uint32_t m, uint32_t* skey,
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// Element types of a score row, read 16 bytes at a time: fp32, or bf16 (its
+// bit pattern, the top half of the fp32 it denotes exactly). bits() gives the
+// fp32 pattern of element j of a load, so keys, survivors and selection are
+// the fp32 ones for both.
+struct F32Elem {
+    typedef f4 Vec;
+    typedef float Scalar;
+    static constexpr int kPerVec = 4;
+    static constexpr int kUnroll = 8;  // loads per lane per round: 32 scores
+    __device__ static uint32_t bits(const Vec& v, int j) { return __float_as_uint(v[j]); }
+    __device__ static uint32_t scalar_bits(Scalar x) { return __float_as_uint(x); }
+};
+struct Bf16Elem {
+    typedef u4 Vec;
+    typedef uint16_t Scalar;
+    static constexpr int kPerVec = 8;
+    static constexpr int kUnroll = 4;  // loads per lane per round: 32 scores
+    __device__ static uint32_t bits(const Vec& v, int j) {
+        return (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
+    }
+    __device__ static uint32_t scalar_bits(Scalar x) { return (uint32_t)x << 16; }
+};
+
+template <class E>
+__device__ __forceinline__ uint32_t elem_key(uint32_t bits) { return order_key(__uint_as_float(bits)); }
+
+// Every score of a row in global memory (the full-row selection's source).
+template <class S, class E>
+struct ElemRowSource {
+    const typename E::Scalar* row;
+    int64_t len;
+    template <class F>
+    __device__ void for_each(F&& f) const {
+        const typename E::Vec* rv = reinterpret_cast<const typename E::Vec*>(row);
+        const int64_t nvec = len / E::kPerVec;
+        for (int64_t v = S::rank(); v < nvec; v += S::kSize) {
+            const typename E::Vec x = rv[v];
+#pragma unroll
+            for (int j = 0; j < E::kPerVec; ++j)
+                f(elem_key<E>(E::bits(x, j)), (uint32_t)(E::kPerVec * v + j));
+        }
+        for (int64_t i = E::kPerVec * nvec + S::rank(); i < len; i += S::kSize)
+            f(elem_key<E>(E::scalar_bits(row[i])), (uint32_t)i);
+    }
+};
+
+// The cutoff key of a row from its sample: `runs` runs of 64 contiguous
+// scores at evenly spaced offsets over [0, L). When the sample has fewer than
+// `want` keys above the row's m-th largest, fewer than m scores can be at or
+// above T; the rank is set so that this is a six-sigma event: the number of
+// sample keys at or above the m-th largest score is binomial with mean
+// mu = m n / L, and want = ceil(mu + 6 sqrt(mu) + 4). T is the lowest key of
+// the want-th largest sample key's top 22 bits (two 11-bit digits), so at
+// most that key and at most 2^10 keys (1/8192 of a binade) below it.
+template <class E>
+__device__ uint32_t short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, uint32_t* skey,
                                  SelectLds lds) {
     using B = BlockScope<kThreads>;
     const int64_t fit = L / (2 * kRunLen);
     const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
-    if (runs < 2) return 0u;  // too short to sample: keep every score
-    const int nsv = runs * (kRunLen / 4);
+    if (runs < 2) return 0u;
+    constexpr int kVecPerRun = kRunLen / E::kPerVec;
+    constexpr int kPer = kMaxSample / E::kPerVec / kThreads;  // loads per lane, all in flight
+    const int nsv = runs * kVecPerRun;
     const int64_t span = L - kRunLen;
-    const float4* row = reinterpret_cast<const float4*>(p.scores + b * p.row_stride);
-    constexpr int kPer = kMaxSample / 4 / kThreads;  // groups per thread, all loads in flight
-    float4 x[kPer];
+    const typename E::Vec* rv = reinterpret_cast<const typename E::Vec*>(row);
+    typename E::Vec x[kPer];
 #pragma unroll
     for (int h = 0; h < kPer; ++h) {
         const int t = h * kThreads + (int)threadIdx.x;
-        const int r = t / (kRunLen / 4);
-        // run r starts at floor(r * span / (runs - 1)), rounded down to a group
-        const int64_t start = ((int64_t)r * span / (runs - 1)) >> 2;
-        x[h] = t < nsv ? row[start + t % (kRunLen / 4)] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const int r = t / kVecPerRun;
+        // run r starts at floor(r * span / (runs - 1)), rounded down to a load
+        const int64_t start = ((int64_t)r * span / (runs - 1)) / E::kPerVec;
+        if (t < nsv) x[h] = rv[start + t % kVecPerRun];
     }
 #pragma unroll
     for (int h = 0; h < kPer; ++h) {
         const int t = h * kThreads + (int)threadIdx.x;
         if (t < nsv) {
-            skey[4 * t + 0] = order_key(x[h].x);
-            skey[4 * t + 1] = order_key(x[h].y);
-            skey[4 * t + 2] = order_key(x[h].z);
-            skey[4 * t + 3] = order_key(x[h].w);
+#pragma unroll
+            for (int j = 0; j < E::kPerVec; ++j) skey[E::kPerVec * t + j] = elem_key<E>(E::bits(x[h], j));
         }
     }
     B::sync();
-    const uint32_t n = 4u * (uint32_t)nsv;
+    const uint32_t n = (uint32_t)(E::kPerVec * nsv);
     const float mu = (float)m * (float)n / (float)L;
     const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
     if (wantf >= (float)n) return 0u;
-    const uint32_t want = (uint32_t)wantf;
-    // two 11-bit digits: the want-th largest sample key's top 22 bits (or a
-    // lower edge at which exactly `want` keys start); T is that prefix's
-    // lowest key, so at most the want-th largest sample key, and at most
-    // 2^10 keys (1/8192 of a binade) below it
     constexpr int kDropBits = 32 - 2 * kDigitBits;
-    return radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, want, 0u, 2 * kDigitBits, n).value
+    return radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, (uint32_t)wantf, 0u, 2 * kDigitBits, n)
+               .value
            << kDropBits;
 }
+
+// ----------------------------------------------------------------------------
+// split rows, launch 1: direct rows, cutoffs and headers
+// ----------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kThreads) void split_sample_kernel(SplitParams p) {
     using B = BlockScope<kThreads>;
@@ -198,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void split_sample_kernel(SplitParams p) {
         kind = kKindAll;
     } else {
         kind = kKindSampled;
-        T = split_cutoff(p, b, L, m, skey, SelectLds{hist, found});
+        T = short_cutoff<F32Elem>(p.scores + b * p.row_stride, L, m, skey, SelectLds{hist, found});
     }
     if (threadIdx.x == 0) p.head[b] = SplitHead{0u, 0u, T, kind};
 }
@@ -355,97 +405,6 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
 // average (the sample's rank rule), so overflow needs a row far from its
 // sample's picture; it then takes the full-row selection.
 constexpr int kShortCap = 3840;
-
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-
-// Element types of a score row, read 16 bytes at a time: fp32, or bf16 (its
-// bit pattern, the top half of the fp32 it denotes exactly). bits() gives the
-// fp32 pattern of element j of a load, so keys, survivors and selection are
-// the fp32 ones for both.
-struct F32Elem {
-    typedef f4 Vec;
-    typedef float Scalar;
-    static constexpr int kPerVec = 4;
-    static constexpr int kUnroll = 8;  // loads per lane per round: 32 scores
-    __device__ static uint32_t bits(const Vec& v, int j) { return __float_as_uint(v[j]); }
-    __device__ static uint32_t scalar_bits(Scalar x) { return __float_as_uint(x); }
-};
-struct Bf16Elem {
-    typedef u4 Vec;
-    typedef uint16_t Scalar;
-    static constexpr int kPerVec = 8;
-    static constexpr int kUnroll = 4;  // loads per lane per round: 32 scores
-    __device__ static uint32_t bits(const Vec& v, int j) {
-        return (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
-    }
-    __device__ static uint32_t scalar_bits(Scalar x) { return (uint32_t)x << 16; }
-};
-
-template <class E>
-__device__ __forceinline__ uint32_t elem_key(uint32_t bits) { return order_key(__uint_as_float(bits)); }
-
-// Every score of a row in global memory (the full-row selection's source).
-template <class S, class E>
-struct ElemRowSource {
-    const typename E::Scalar* row;
-    int64_t len;
-    template <class F>
-    __device__ void for_each(F&& f) const {
-        const typename E::Vec* rv = reinterpret_cast<const typename E::Vec*>(row);
-        const int64_t nvec = len / E::kPerVec;
-        for (int64_t v = S::rank(); v < nvec; v += S::kSize) {
-            const typename E::Vec x = rv[v];
-#pragma unroll
-            for (int j = 0; j < E::kPerVec; ++j)
-                f(elem_key<E>(E::bits(x, j)), (uint32_t)(E::kPerVec * v + j));
-        }
-        for (int64_t i = E::kPerVec * nvec + S::rank(); i < len; i += S::kSize)
-            f(elem_key<E>(E::scalar_bits(row[i])), (uint32_t)i);
-    }
-};
-
-// The cutoff key of a short row from its sample: `runs` runs of 64 scores at
-// evenly spaced offsets, the same rank rule as the split-row mode, two 11-bit
-// digits (T at most 2^10 keys below the wanted sample key).
-template <class E>
-__device__ uint32_t short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, uint32_t* skey,
-                                 SelectLds lds) {
-    using B = BlockScope<kThreads>;
-    const int64_t fit = L / (2 * kRunLen);
-    const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
-    if (runs < 2) return 0u;
-    constexpr int kVecPerRun = kRunLen / E::kPerVec;
-    constexpr int kPer = kMaxSample / E::kPerVec / kThreads;  // loads per lane, all in flight
-    const int nsv = runs * kVecPerRun;
-    const int64_t span = L - kRunLen;
-    const typename E::Vec* rv = reinterpret_cast<const typename E::Vec*>(row);
-    typename E::Vec x[kPer];
-#pragma unroll
-    for (int h = 0; h < kPer; ++h) {
-        const int t = h * kThreads + (int)threadIdx.x;
-        const int r = t / kVecPerRun;
-        // run r starts at floor(r * span / (runs - 1)), rounded down to a load
-        const int64_t start = ((int64_t)r * span / (runs - 1)) / E::kPerVec;
-        if (t < nsv) x[h] = rv[start + t % kVecPerRun];
-    }
-#pragma unroll
-    for (int h = 0; h < kPer; ++h) {
-        const int t = h * kThreads + (int)threadIdx.x;
-        if (t < nsv) {
-#pragma unroll
-            for (int j = 0; j < E::kPerVec; ++j) skey[E::kPerVec * t + j] = elem_key<E>(E::bits(x[h], j));
-        }
-    }
-    B::sync();
-    const uint32_t n = (uint32_t)(E::kPerVec * nsv);
-    const float mu = (float)m * (float)n / (float)L;
-    const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
-    if (wantf >= (float)n) return 0u;
-    constexpr int kDropBits = 32 - 2 * kDigitBits;
-    return radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, (uint32_t)wantf, 0u, 2 * kDigitBits, n)
-               .value
-           << kDropBits;
-}
 
 template <class E>
 __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) {

@@ -280,18 +280,38 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
     }
     B::sync();
     if (threadIdx.x < 64) {  // suffix sums of the bucket counts, 32 buckets per lane
+        // the lane's counts in registers (8 16-byte LDS reads issued together),
+        // its starts written back the same way: interleaved single reads and
+        // writes of LDS would each wait for the one before
         const uint32_t lane = lane_id();
-        const uint32_t* c = cnt + 32 * lane;
+        const uint4* c4 = reinterpret_cast<const uint4*>(cnt + 32 * lane);
+        uint32_t c[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint4 v = c4[q];
+            c[4 * q + 0] = v.x;
+            c[4 * q + 1] = v.y;
+            c[4 * q + 2] = v.z;
+            c[4 * q + 3] = v.w;
+        }
         uint32_t own = 0;
+#pragma unroll
         for (int j = 0; j < 32; ++j) own += c[j];
         const uint32_t incl = wave_inclusive_sum(own);
         const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
         uint32_t above = total - incl;  // rows in the buckets of higher lanes
+        uint32_t sv[32];
+#pragma unroll
         for (int j = 31; j >= 0; --j) {
-            start[32 * lane + j] = above;
+            sv[j] = above;
             above += c[j];
-            if (c[j] > (uint32_t)kHeavyBucket) sm.heavy[atomicAdd(&sm.nheavy, 1u)] = 32 * lane + j;
         }
+        uint4* s4 = reinterpret_cast<uint4*>(start + 32 * lane);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s4[q] = make_uint4(sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]);
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            if (c[j] > (uint32_t)kHeavyBucket) sm.heavy[atomicAdd(&sm.nheavy, 1u)] = 32 * lane + j;
         if (lane == 0) sm.nqueue = total;
     }
     B::sync();

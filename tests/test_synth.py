@@ -74,3 +74,40 @@ def test_c5_categories_and_page_table():
         assert np.array_equal(np.sort(wl.page_table[b]), np.arange(64))
     pool = synth.c5(batch=8, width=4096, global_pool=True)
     assert np.unique(pool.page_table).size == pool.page_table.size
+
+
+def test_bf16_rounding_is_nearest_even():
+    # values exactly between two bf16 numbers go to the even pattern; NaN
+    # becomes the quiet NaN; overflow past the largest bf16 rounds to +inf
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -7, -2.5, 3.4e38, np.nan],
+                 np.float32)
+    got = synth.to_bf16_bits(x)
+    assert got.tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x7F80, 0x7FC0]
+
+
+def test_bf16_workloads():
+    a, b = synth.bf16_rows(64, 16384, 2048), synth.bf16_rows(64, 16384, 2048)
+    assert digest(a.bits) == digest(b.bits) and digest(a.page_table) == digest(b.page_table)
+    assert a.bits.dtype == np.uint16 and a.bits.shape == (64, 16384)
+    assert np.all((a.lengths >= int(np.ceil(0.8 * 16384))) & (a.lengths <= 16384))
+    for r in range(a.batch):
+        L = int(a.lengths[r])
+        assert np.all(a.bits[r, L:] == synth.BF16_POISON)
+        assert not np.any((a.bits[r, :L] & 0x7FFF) > 0x7F80)  # no NaN inside the row
+        assert sorted(a.page_table[r].tolist()) == list(range(16384 // 64))
+    adv = synth.bf16_adversarial(512)
+    assert adv.bits.shape == (2 * len(synth.C2_KINDS), 16384)
+
+
+def test_amax8_and_block_table_workloads():
+    w = synth.amax8_rows(16, 4096, 64, nan_rate=0.01, zero_rate=0.01)
+    assert w.out_blocks == 512 and w.scores.shape == (16, 4096)
+    inside = np.concatenate([w.scores[r, :int(w.lengths[r])] for r in range(16)])
+    assert np.isnan(inside).any() and (inside == 0).any()  # NaN and zeros inside the rows
+    c = synth.candidate_blocks(128, 8192, 32, page_size=64)
+    for r in range(c.batch):
+        nb = -(-max(int(c.lengths[r]), 0) // 8)
+        if nb > 32:  # a top-k selection: 32 distinct ids of [0, nb)
+            row = c.blocks[r]
+            assert len(set(row.tolist())) == 32 and row.min() >= 0 and row.max() < nb
+    assert c.page_table.shape == (128, 8192 // 8 // 8)

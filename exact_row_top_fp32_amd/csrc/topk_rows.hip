@@ -221,7 +221,8 @@ __device__ __forceinline__ void defer_row(const Params& p, Shared& sm, SelectLds
 // the queue
 // ----------------------------------------------------------------------------
 
-// Whole workgroup, at start: rows with L <= k (dealt round-robin) are written
+// Whole workgroup, at start: with no more rows than workgroups, workgroup w
+// takes row w. Otherwise rows with L <= k (dealt round-robin) are written
 // out directly. When every workgroup's share fits one table, the other rows
 // are put in a longest-first order (a counting sort over 2048 length buckets,
 // ties by row index, the same in every workgroup) and this workgroup's share
@@ -230,6 +231,24 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
     using B = BlockScope<kThreads>;
     const int64_t batch = p.batch;
     const uint32_t G = gridDim.x;
+    if (batch <= (int64_t)G) {
+        // no more rows than workgroups (the grid is min(batch, CUs)):
+        // workgroup w takes row w alone, so there is no order to compute
+        const int64_t b = blockIdx.x;
+        const int64_t L = row_len(p, b);
+        if (L <= p.k) direct_row<B>(p, b, L);
+        if (threadIdx.x == 0) {
+            sm.ordered = 1u;
+            sm.nqueue = L > p.k ? 1u : 0u;
+            sm.tab_n = L > p.k ? 1u : 0u;
+            sm.tab_pos = 0u;
+            sm.tab_round = 0u;
+            sm.tab_b[0] = (int32_t)b;
+            sm.tab_len[0] = (int32_t)L;
+        }
+        B::sync();
+        return;
+    }
     if (batch > kOrderMaxRows || batch > (int64_t)kTable * G) {
         for (int64_t b = blockIdx.x; b < batch; b += G) {
             const int64_t L = row_len(p, b);

@@ -1295,8 +1295,8 @@ int topk_select_ex(const float* scores, int64_t batch, int64_t row_stride, int64
     if (batch > 1 && (row_stride & 3) != 0) return TOPK_ERR_ALIGN;
     // short rows on the automatic path: one workgroup per row, survivors in
     // LDS, the hardware scheduler filling the compute units
-    if (n_cols <= kShortMaxCols && opt.force_path == TOPK_PATH_AUTO && opt.capacity == kCapacity &&
-        (options == nullptr || options->capacity == 0))
+    if (n_cols <= kShortMaxCols && batch <= kShortMaxBatch && opt.force_path == TOPK_PATH_AUTO &&
+        opt.capacity == kCapacity && (options == nullptr || options->capacity == 0))
         return launch_short_rows(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
                                  page_table_stride, page_size, opt.row_stats, static_cast<hipStream_t>(hip_stream));
     const int cus = device_cus();

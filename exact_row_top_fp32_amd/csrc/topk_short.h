@@ -14,6 +14,11 @@ namespace topk {
 #endif
 constexpr int64_t kShortMaxCols = TOPK_SHORT_MAX_COLS;
 
+// Most rows one short-row launch takes (one 256-thread workgroup per row, a
+// grid of at most 2^32 - 1 work-items); larger batches go to the persistent
+// kernel.
+constexpr int64_t kShortMaxBatch = 0xFFFFFFFFll / 256;
+
 // One workgroup per row: sample, one streaming pass into an LDS survivor
 // buffer, exact selection there (full-row selection on overflow or
 // underflow). Arguments as for topk_select; the caller has checked them.

@@ -199,6 +199,7 @@ int32_t topk_split_capacity(void);
  *  scores     bf16 bit patterns [batch, row_stride]; 16-byte aligned base
  *             and row_stride % 8 == 0 (when batch > 1)
  *  n_cols     at most 16384 (TOPK_ERR_ARG above)
+ *  batch      at most 16777215 (one 256-thread workgroup per row; TOPK_ERR_ARG above)
  * Other arguments, results and status codes as for topk_select.
  */
 int topk_select_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, int64_t n_cols,

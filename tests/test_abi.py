@@ -170,6 +170,7 @@ def test_indexer_host_argument_checks(lib):
     assert bf(n_cols=16385, stride=16392) == 1 and bf(k=2049) == 2 and bf(k=0) == 2
     assert bf(s=FAKE + 2) == 3 and bf(stride=1028) == 3 and bf(out=None) == 1
     assert bf(batch=0, s=None, out=None) == 0
+    assert bf(batch=2**24) == 1  # past one 256-thread workgroup per row
 
     lib.amax8_varlen.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,

@@ -419,3 +419,41 @@ def test_short_rows_overflow_fallback(topk):
     paths = dict(zip(*np.unique(stats[:, 0], return_counts=True)))
     say("  short-row paths on the adversarial rows:", paths)
     assert paths.get(4, 0) > 0, "some adversarial row overflows the buffer"
+
+
+@pytest.mark.parametrize("W", [20000, 40000], ids=["short_rows", "persistent"])
+@pytest.mark.parametrize("page_size", [1, 3, 100, 4096])
+def test_page_sizes(topk, W, page_size):
+    # page sizes that are not powers of two, one and larger than some rows;
+    # page-table slots offset per row so a row-mixing mistake shows
+    k = 777
+    kinds = ["normal", "heavy_ties", "signed_zero", "neginf_few_finite", "ascending", "clustered_peaks"]
+    wl = synth.mixed_rows(kinds, W, k, seed=37)
+    wl.lengths = np.array([W, W - 1, 5000, k + 1, k - 1, 4099], np.int32)
+    synth.poison_tails(wl.scores, wl.lengths)
+    pages = -(-W // page_size)
+    rng = np.random.default_rng(38)
+    wl.page_table = np.stack([rng.permutation(pages) + 7 * pages * b for b in range(wl.batch)]).astype(np.int32)
+    wl.page_size = page_size
+    got, _ = run(topk, wl)
+    assert_parity(wl, got, expect(wl))
+
+
+@pytest.mark.parametrize("page_size", [1, 3, 100])
+def test_bf16_page_sizes(topk, page_size):
+    W, k = 16384, 500
+    rng = np.random.default_rng(39)
+    bits = synth.to_bf16_bits(rng.standard_normal((5, W)).astype(np.float32))
+    lengths = np.array([W, 9000, k + 1, k, 3], np.int32)
+    synth.poison_tails_bf16(bits, lengths)
+    pages = -(-W // page_size)
+    pt = np.stack([rng.permutation(pages) + 5 * pages * b for b in range(5)]).astype(np.int32)
+    wl = synth.Bf16Workload("bf16_pages", 39, bits, lengths, W, k, pt, page_size)
+    s = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    out = topk.topk_select_bf16(s, torch.from_numpy(lengths).cuda(), k, None, torch.from_numpy(pt).cuda(),
+                                page_size)
+    torch.cuda.synchronize()
+    want = oracle.topk_bf16(bits, lengths, k, page_table=pt, page_size=page_size)
+    fails = check(oracle.bf16_to_f32(bits), lengths, W, k, out.cpu().numpy(), want, page_table=pt,
+                  page_size=page_size)
+    assert not fails, "\n".join(fails)

@@ -1089,6 +1089,110 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
     }
 }
 
+// Slots for every lane's `cnt` entries from an LDS counter: one atomic per
+// wave; every lane of the wave active.
+__device__ __forceinline__ uint32_t wave_reserve_count(uint32_t* counter, uint32_t cnt) {
+    const uint32_t incl = wave_inclusive_sum(cnt);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    uint32_t base = 0u;
+    if (total != 0u) {
+        if (lane_id() == 0) base = atomicAdd(counter, total);
+        base = __builtin_amdgcn_readfirstlane(base);
+    }
+    return base + incl - cnt;
+}
+
+// The whole workgroup's finish of a row (its last row): the selection of
+// finish_sampled with each lane's survivors read from LDS once, into
+// registers, for both passes, and one slot reservation per wave: the entries
+// above the cutoff bin take slots [0, above), the cutoff bin's best `need`
+// the slots [m - need, m). Row stats and counters as finish_sampled.
+template <class S, bool kNonNegT>
+__device__ __forceinline__ void finish_sampled_wg(const Params& p, Shared& sm, const RowSlot& R, int x, uint32_t n,
+                                                  SelectLds lds) {
+    constexpr int kPer = (kCapacity + S::kSize - 1) / S::kSize;  // entries per lane at most
+    const uint32_t m = R.m;
+    const uint2* E = sm.surv[x];
+    auto val = [](uint32_t bits) -> uint32_t {
+        if constexpr (kNonNegT) return bits;
+        else return order_key(__uint_as_float(bits));
+    };
+    constexpr uint32_t kShift = kNonNegT ? 0x80000000u : 0u;  // key = val + kShift
+    const uint32_t Tv = R.T - kShift;
+    const uint32_t sh = R.sh;
+    uint2 v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {  // every load issued before any is used
+        const uint32_t e = S::rank() + (uint32_t)j * S::kSize;
+        v[j] = e < n ? E[e] : make_uint2(0u, 0u);
+    }
+    uint32_t vm = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        if (S::rank() + (uint32_t)j * S::kSize < n) {
+            const uint32_t kv = val(v[j].x);
+            vm = max(vm, kv);
+            const uint32_t d = (kv - Tv) >> sh;
+            atomicAdd(&lds.hist[d < (uint32_t)kBins ? d : (uint32_t)kBins - 1u], 1u);
+        }
+    }
+    vm = wave_max(vm);
+    if (lane_id() == 0) atomicMax(&sm.vmax[x], vm + kShift);
+    S::sync();
+    const Found f = find_rank_bin<S>(lds, m);
+    if (f.count > (uint32_t)kMaxCand || f.digit == (uint32_t)kBins - 1u) {
+        const PairSource<S> src{E, n};
+        const Selection s = select_top<S>(lds, src, m, n, R.T, sm.vmax[x], bits_for(R.L));
+        OutRow out = out_row(p, R.b, m, &sm.emitted);
+        emit(src, s, out);
+        return;
+    }
+    const uint32_t need = m - f.above;
+    const bool whole = f.count == need;
+    const uint64_t hi = (uint64_t)R.T + ((uint64_t)(f.digit + 1u) << sh);
+    const uint32_t t_above = (hi > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)(hi - 1u)) - kShift;
+    const uint32_t t_lo = R.T + (f.digit << sh) - kShift;
+    const uint32_t t_take = whole ? t_lo : t_above + 1u;
+    const bool take_none = !whole && t_above == 0xFFFFFFFFu;
+    const uint32_t c_span = t_above - t_lo;
+    uint32_t tmask = 0u, cmask = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const bool ok = S::rank() + (uint32_t)j * S::kSize < n;
+        const uint32_t kv = val(v[j].x);
+        tmask |= (uint32_t)(ok & !take_none & (kv >= t_take)) << j;
+        cmask |= (uint32_t)(ok & !whole & (kv - t_lo <= c_span)) << j;
+    }
+    uint32_t ts = wave_reserve_count(&sm.emitted, (uint32_t)__popc(tmask));
+    uint32_t cs = wave_reserve_count(&sm.ncand, (uint32_t)__popc(cmask));
+    const OutRow out = out_row(p, R.b, m, nullptr);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        if ((tmask >> j) & 1u) {
+            if (ts < m) out.row[ts] = out.map(v[j].y);
+            ++ts;
+        }
+        if ((cmask >> j) & 1u) {
+            if (cs < (uint32_t)kMaxCand) {
+                sm.cand_key[cs] = val(v[j].x);
+                sm.cand_idx[cs] = v[j].y;
+            }
+            ++cs;
+        }
+    }
+    if (whole) return;
+    S::sync();
+    if (S::first_wave()) {
+        const uint32_t lane = lane_id();
+        const uint32_t nc = f.count;
+        const bool have = lane < nc;
+        const uint32_t kj = have ? sm.cand_key[lane] : 0u;
+        const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
+        const uint32_t r = rank_in_wave(kj, ij, nc);
+        if (have && r < need) out.row[m - need + r] = out.map(ij);
+    }
+}
+
 // Scope S: finishes row R from buffer x, or defers it to the full-row path
 // when its survivors overflowed the buffer or fell short of m. Leaves buffer
 // x's counters and histogram zero.
@@ -1100,8 +1204,13 @@ __device__ __forceinline__ void finish_row(const Params& p, Shared& sm, const Ro
         const int code = n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
         if (S::first_wave()) defer_row(p, sm, lds, &sm.emitted, R.b, code);
     } else {
-        if (R.T >= 0x80000000u) finish_sampled<S, true>(p, sm, R, x, n, lds);
-        else finish_sampled<S, false>(p, sm, R, x, n, lds);
+        if constexpr (S::kSize == 64) {
+            if (R.T >= 0x80000000u) finish_sampled<S, true>(p, sm, R, x, n, lds);
+            else finish_sampled<S, false>(p, sm, R, x, n, lds);
+        } else {
+            if (R.T >= 0x80000000u) finish_sampled_wg<S, true>(p, sm, R, x, n, lds);
+            else finish_sampled_wg<S, false>(p, sm, R, x, n, lds);
+        }
         if (S::rank() == 0) put_stats(p, R.b, R.kind == kKindAll ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED, n);
     }
     S::sync();

@@ -93,6 +93,20 @@ __device__ __forceinline__ uint32_t wave_reserve(uint32_t* counter, bool pred) {
     return base + lanes_below(mask);
 }
 
+// Slots for every lane's `cnt` entries from a counter (LDS or device
+// memory): one atomic per wave, lanes placed by a wave prefix sum. Every lane
+// of the wave must be active.
+__device__ __forceinline__ uint32_t wave_reserve_count(uint32_t* counter, uint32_t cnt) {
+    const uint32_t incl = wave_inclusive_sum(cnt);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    uint32_t base = 0u;
+    if (total != 0u) {
+        if (lane_id() == 0) base = atomicAdd(counter, total);
+        base = __builtin_amdgcn_readfirstlane(base);
+    }
+    return base + incl - cnt;
+}
+
 __device__ __forceinline__ f4 load_nt(const f4* p) { return __builtin_nontemporal_load(p); }
 
 // ----------------------------------------------------------------------------

@@ -35,8 +35,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include "exact_topk.h"
 #include "topk_device.h"
 #include "topk_short.h"
@@ -1089,19 +1087,6 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
     }
 }
 
-// Slots for every lane's `cnt` entries from an LDS counter: one atomic per
-// wave; every lane of the wave active.
-__device__ __forceinline__ uint32_t wave_reserve_count(uint32_t* counter, uint32_t cnt) {
-    const uint32_t incl = wave_inclusive_sum(cnt);
-    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
-    uint32_t base = 0u;
-    if (total != 0u) {
-        if (lane_id() == 0) base = atomicAdd(counter, total);
-        base = __builtin_amdgcn_readfirstlane(base);
-    }
-    return base + incl - cnt;
-}
-
 // The whole workgroup's finish of a row (its last row): the selection of
 // finish_sampled with each lane's survivors read from LDS once, into
 // registers, for both passes, and one slot reservation per wave: the entries
@@ -1339,20 +1324,6 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     const uint32_t nd = sm.ndeferred < (uint32_t)kMaxDeferred ? sm.ndeferred : (uint32_t)kMaxDeferred;
     for (uint32_t j = 0; j < nd; ++j)
         full_row<B>(p, SelectLds{sm.hist[0], sm.found}, &sm.emitted, sm.deferred[j], sm.deferred_code[j]);
-}
-
-int device_cus() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (dev >= 0 && dev < 64) {
-        const int v = cached[dev].load(std::memory_order_relaxed);
-        if (v > 0) return v;
-    }
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
-    return n;
 }
 
 }  // namespace

@@ -1,11 +1,29 @@
-// The short-row selection kernel's launchers, shared between translation units
-// of the library (not part of the C ABI).
+// Launch-side pieces shared between the library's translation units (not
+// part of the C ABI): the current device's compute-unit count and the
+// short-row selection kernel's launchers.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace topk {
+
+// Compute units of the current device (cached per device), 0 on error.
+inline int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 64) {
+        const int v = cached[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 // Widest rows the short-row kernel takes: the automatic path of topk_select
 // routes batches whose n_cols is at most this to it.

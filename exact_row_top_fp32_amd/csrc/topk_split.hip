@@ -41,8 +41,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
-
 #include "exact_topk.h"
 #include "topk_device.h"
 #include "topk_short.h"
@@ -257,19 +255,6 @@ __global__ __launch_bounds__(kThreads) void split_sample_kernel(SplitParams p) {
 // launch 2: pieces append their survivors
 // ----------------------------------------------------------------------------
 
-// Survivor slots for every lane's `cnt` hits: one device-scope atomic per
-// wave; every lane of the wave must be active.
-__device__ __forceinline__ uint32_t wave_reserve_n(uint32_t* counter, uint32_t cnt) {
-    const uint32_t incl = wave_inclusive_sum(cnt);
-    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
-    uint32_t base = 0u;
-    if (total != 0u) {
-        if (lane_id() == 0) base = atomicAdd(counter, total);
-        base = __builtin_amdgcn_readfirstlane(base);
-    }
-    return base + incl - cnt;
-}
-
 __device__ __forceinline__ void load_round(const f4* r4, int64_t base, int64_t g1, f4 (&x)[kUnroll]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -287,7 +272,7 @@ __device__ __forceinline__ void filter_round(const f4 (&x)[kUnroll], int64_t bas
 #pragma unroll
         for (int j = 0; j < 4; ++j) cnt += (in && order_key(x[u][j]) >= T) ? 1u : 0u;
     }
-    uint32_t slot = wave_reserve_n(&h->count, cnt);
+    uint32_t slot = wave_reserve_count(&h->count, cnt);
     if (cnt != 0u) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -330,7 +315,7 @@ __device__ __forceinline__ void stream_piece(const SplitParams& p, int64_t b, in
         const int64_t i = nvec * 4 + threadIdx.x;
         const float v = i < L ? row[i] : 0.0f;
         const bool hit = i < L && order_key(v) >= T;
-        const uint32_t slot = wave_reserve_n(&h->count, hit ? 1u : 0u);
+        const uint32_t slot = wave_reserve_count(&h->count, hit ? 1u : 0u);
         if (hit && slot < cap) surv[slot] = make_uint2(__float_as_uint(v), (uint32_t)i);
     }
 }
@@ -457,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
 #pragma unroll
             for (int j = 0; j < E::kPerVec; ++j) cnt += (in && elem_key<E>(E::bits(x[u], j)) >= T) ? 1u : 0u;
         }
-        uint32_t slot = wave_reserve_n(&count, cnt);
+        uint32_t slot = wave_reserve_count(&count, cnt);
         if (cnt != 0u) {
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
@@ -489,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         const int64_t i = nvec * E::kPerVec + threadIdx.x;
         const uint32_t bits = i < L ? E::scalar_bits(row[i]) : 0u;
         const bool hit = i < L && elem_key<E>(bits) >= T;
-        const uint32_t slot = wave_reserve_n(&count, hit ? 1u : 0u);
+        const uint32_t slot = wave_reserve_count(&count, hit ? 1u : 0u);
         if (hit && slot < (uint32_t)kShortCap) buf[slot] = make_uint2(bits, (uint32_t)i);
     }
     B::sync();
@@ -508,20 +493,6 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         emit(src, s, out);
     }
     if (threadIdx.x == 0) split_stats(p, b, code, n);
-}
-
-int split_device_cus() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (dev >= 0 && dev < 64) {
-        const int v = cached[dev].load(std::memory_order_relaxed);
-        if (v > 0) return v;
-    }
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
-    return n;
 }
 
 }  // namespace
@@ -594,7 +565,7 @@ int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, in
     // piece a whole number of load rounds
     int64_t want = pieces;
     if (want == 0) {
-        const int cus = split_device_cus();
+        const int cus = device_cus();
         if (cus <= 0) return TOPK_ERR_LAUNCH;
         want = (4 * (int64_t)cus + batch - 1) / batch;
     }

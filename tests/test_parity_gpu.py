@@ -457,3 +457,70 @@ def test_bf16_page_sizes(topk, page_size):
     fails = check(oracle.bf16_to_f32(bits), lengths, W, k, out.cpu().numpy(), want, page_table=pt,
                   page_size=page_size)
     assert not fails, "\n".join(fails)
+
+
+# ----------------------------------------------------------------------------
+# a sample that sees only the peaks: survivors fall short of m
+# ----------------------------------------------------------------------------
+
+def sample_positions(L):
+    """Where every sampling path reads a row of length L: runs of 64 scores at
+    floor(r (L - 64) / (runs - 1)) rounded down to a multiple of 4,
+    runs = min(L // 128, 64)."""
+    runs = min(L // 128, 64)
+    pos = []
+    for r in range(runs):
+        start = (r * (L - 64) // (runs - 1)) & ~3
+        pos.extend(range(start, start + 64))
+    return np.array(pos, np.int64)
+
+
+@pytest.mark.parametrize("W,k", [(20000, 512), (131072, 2048), (131072, 512)],
+                         ids=["short_rows", "persistent_k2048", "persistent_k512"])
+def test_sample_that_sees_only_peaks_underflows(topk, W, k):
+    # peaks planted on sampled positions only, fewer than m of them: the
+    # sampled cutoff lands among the peaks, fewer than m scores survive, and
+    # the full-row selection must take over (the pages' sampled-peaks case)
+    rng = np.random.default_rng(40)
+    B = 4
+    scores = rng.standard_normal((B, W)).astype(np.float32)
+    lengths = np.array([W, W - 3, W - 17, W], np.int32)
+    for b in range(B):
+        pos = sample_positions(int(lengths[b]))
+        hit = rng.choice(pos, min(k // 2, pos.size), replace=False)
+        scores[b, hit] = (50.0 + rng.standard_normal(hit.size)).astype(np.float32)
+    synth.poison_tails(scores, lengths)
+    wl = synth.Workload("sampled_peaks", 40, scores, lengths, W, k)
+    want = expect(wl)
+    got, stats = run(topk, wl, want_stats=True)
+    assert_parity(wl, got, want)
+    assert np.all(stats[:, 0] == 5), f"every row must take the underflow fallback: {stats[:, 0]}"
+    if W > 16384:
+        got, stats = run(topk, wl, force=2, want_stats=True)
+        assert_parity(wl, got, want)
+        assert np.all(stats[:, 0] == 5)
+    # the split-row entry samples the same positions
+    buf = torch.full((B, k), CANARY, dtype=torch.int32, device="cuda")
+    sstats = torch.full((B, 2), -7, dtype=torch.int32, device="cuda")
+    topk.topk_select_split(to_dev(wl.scores), to_dev(wl.lengths), k, buf, row_stats=sstats)
+    torch.cuda.synchronize()
+    assert_parity(wl, buf.cpu().numpy(), want)
+    assert np.all(sstats.cpu().numpy()[:, 0] == 5)
+
+
+@pytest.mark.parametrize("W", [20000, 131072])
+def test_permuted_rows_select_the_same_values(topk, W):
+    # the same multiset under a random permutation: the same selected values
+    k = 1024
+    wl = synth.mixed_rows(["heavy_ties", "onebin", "crowd4096", "signed_zero", "neginf_half", "normal"], W, k,
+                          seed=41)
+    rng = np.random.default_rng(42)
+    perm = np.stack([rng.permutation(W) for _ in range(wl.batch)])
+    pw = synth.Workload("permuted", 42, np.take_along_axis(wl.scores, perm, axis=1), wl.lengths, W, k)
+    a, _ = run(topk, wl)
+    b, _ = run(topk, pw)
+    bits = wl.scores.view(np.uint32)
+    pbits = pw.scores.view(np.uint32)
+    for r in range(wl.batch):
+        assert np.array_equal(np.sort(bits[r, a[r]]), np.sort(pbits[r, b[r]]))
+    assert_parity(pw, b, expect(pw))

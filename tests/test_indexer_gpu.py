@@ -211,8 +211,17 @@ def test_block_table_junk_entries_and_large_rows(topk):
 # the two-level indexer, chained
 # ----------------------------------------------------------------------------
 
+def test_amax8_on_the_bench_batch(topk, c3):
+    # the block max exactly as the bench times it: the 1024 x 131072 decode
+    # batch, topk = 512
+    wl = synth.Amax8Workload("amax8_c3", 3, c3.scores, c3.lengths, c3.n_cols // 8, 512)
+    run_amax(topk, wl)
+
+
 def test_two_level_indexer_chain(topk, c3):
-    B, k, ps = 256, 512, 64
+    # the whole decode batch, as the bench chains it, with edge lengths in the
+    # first rows
+    B, k, ps = c3.batch, 512, 64
     scores = c3.scores[:B]
     lengths = c3.lengths[:B].copy()
     lengths[:8] = [0, 1, 7, 8 * k, 8 * k + 1, 100, 4000, 8 * k - 3]

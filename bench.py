@@ -11,8 +11,10 @@ the timed region. `value` is the algorithmic bytes of one step (4 B per valid
 score read, 4 B per length read, 4 B per output slot written) divided by the
 wall time per step, in GB/s.
 
-Besides the step, the same JSON line carries two sections timed after it,
-neither part of `value`: `small_batch` (the first 40 rows of each batch, one
+Besides the step, the same JSON line carries three sections timed after it,
+none part of `value`: `plain_read_context` (a plain row-max read of the same
+score buffers, for how close the selection comes to a bare streaming read),
+`small_batch` (the first 40 rows of each batch, one
 workgroup per row against the split-row entry, eager and replayed from a
 HIP graph) and `indexer` (the bf16 top-k and the two-level indexer's block
 max, block-key top-k and block table, each with its algorithmic bytes and
@@ -214,6 +216,8 @@ def main() -> int:
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic}
 
+    plain = plain_read(wls, d_scores, names, detail, stream) if not args.only else None
+
     small = small_batch(topk, wls, d_scores, d_len, names, args.small_batch, stream) \
         if args.small_batch > 0 and not args.only else None
 
@@ -247,12 +251,33 @@ def main() -> int:
         },
         "detail": detail,
         "roofline": roofline,
+        "plain_read_context": plain,
         "small_batch": small,
         "indexer": indexer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def plain_read(wls, d_scores, names, detail, stream):
+    """Context for the roofline fraction: a plain streaming read of the same
+    score buffers (torch's row max over every column, no selection), its rate,
+    and the selection's warm rate as a fraction of it."""
+    import torch
+
+    res = {}
+    for n in names:
+        w = wls[n]
+        s = d_scores[n][:, :w.n_cols]
+        nbytes = 4 * w.batch * w.n_cols
+        us = time_us(lambda: torch.amax(s, dim=1), stream)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[n] = {"kernel": "torch.amax(scores, dim=1)", "bytes": nbytes, "warm_us_median": round(us, 2),
+                  "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                  "topk_gbs_over_plain_read": round(detail[n]["warm_gbs"] / gbs, 3)}
+    log(f"plain read: {res}")
+    return res
 
 
 def small_batch(topk, wls, d_scores, d_len, names, rows, stream, iters=200):
@@ -451,12 +476,32 @@ def cpu_baseline(wls, d_out, names):
             break
     if not ok:
         raise SystemExit("GPU selection differs from the oracle")
+    # one thread, a few rows of each batch: the per-row cost without the
+    # parallel loop
+    one_thread = {}
+    for n in names:
+        w = wls[n]
+        rows = min(8, w.batch)
+        _, secs = oracle.timed_topk(w.scores[:rows], w.lengths[:rows], w.k, n_cols=w.n_cols, threads=1)
+        one_thread[n] = round(secs / rows * 1e6, 1)
     sample = "; ".join(f"all {wls[n].batch} rows of the {wls[n].batch}x{wls[n].n_cols} k={wls[n].k} batch"
                        for n in names)
     return {"value": round(total_bytes / total_s / 1e9, 3), "unit": "GB/s",
             "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"{sample}, {passes} passes (full sort per row, OpenMP over rows)",
-            "seconds": round(total_s, 3), "gpu_matches_oracle_on_every_row": ok}
+            "seconds": round(total_s, 3), "gpu_matches_oracle_on_every_row": ok,
+            "one_thread_us_per_row": one_thread, "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

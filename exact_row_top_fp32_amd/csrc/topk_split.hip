@@ -178,13 +178,24 @@ struct ElemRowSource {
 // mu = m n / L, and want = ceil(mu + 6 sqrt(mu) + 4). T is the lowest key of
 // the want-th largest sample key's top 22 bits (two 11-bit digits), so at
 // most that key and at most 2^10 keys (1/8192 of a binade) below it.
-template <class E>
+//
+// `issue` runs right after the sample's loads are issued (and on the early
+// return), so that a caller's own loads are in flight while the cutoff is
+// found.
+struct NoIssue {
+    __device__ void operator()() const {}
+};
+
+template <class E, class Issue = NoIssue>
 __device__ uint32_t short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, uint32_t* skey,
-                                 SelectLds lds) {
+                                 SelectLds lds, Issue&& issue = Issue{}) {
     using B = BlockScope<kThreads>;
     const int64_t fit = L / (2 * kRunLen);
     const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
-    if (runs < 2) return 0u;
+    if (runs < 2) {
+        issue();
+        return 0u;
+    }
     constexpr int kVecPerRun = kRunLen / E::kPerVec;
     constexpr int kPer = kMaxSample / E::kPerVec / kThreads;  // loads per lane, all in flight
     const int nsv = runs * kVecPerRun;
@@ -199,6 +210,7 @@ __device__ uint32_t short_cutoff(const typename E::Scalar* row, int64_t L, uint3
         const int64_t start = ((int64_t)r * span / (runs - 1)) / E::kPerVec;
         if (t < nsv) x[h] = rv[start + t % kVecPerRun];
     }
+    issue();
 #pragma unroll
     for (int h = 0; h < kPer; ++h) {
         const int t = h * kThreads + (int)threadIdx.x;
@@ -421,10 +433,10 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     const SelectLds lds{hist, found};
     const typename E::Scalar* row = reinterpret_cast<const typename E::Scalar*>(p.scores) + b * p.row_stride;
     const bool keep_all = L <= kShortCap;
-    const uint32_t T = keep_all ? 0u : short_cutoff<E>(row, L, m, reinterpret_cast<uint32_t*>(buf), lds);
-    B::sync();  // the sample's keys are read; the buffer takes survivors now
 
-    // one streaming pass, two rounds of loads in flight; hits go to LDS
+    // one streaming pass, two rounds of loads in flight; hits go to LDS. A
+    // sampled row's first two rounds are issued right behind the sample's
+    // loads, so that they land while the cutoff is found.
     const int64_t nvec = L / E::kPerVec;
     const Vec* rv = reinterpret_cast<const Vec*>(row);
     auto load = [&](int64_t base, Vec (&x)[kU]) {
@@ -434,6 +446,30 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
             if (g < nvec) x[u] = __builtin_nontemporal_load(rv + g);
         }
     };
+    Vec xa[kU], xc[kU];
+    // Every lane loads; a lane past the row's full loads takes the last one
+    // again (the filter skips it). With a fixed number of loads issued after
+    // the sample's, the sample can be used once its own loads are in, these
+    // still in flight. A sampled row has more than kShortCap scores, so
+    // nvec >= 1.
+    auto first_loads = [&]() {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t g = u * kThreads + threadIdx.x;
+            xa[u] = __builtin_nontemporal_load(rv + (g < nvec ? g : nvec - 1));
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t g = kR + u * kThreads + threadIdx.x;
+            xc[u] = __builtin_nontemporal_load(rv + (g < nvec ? g : nvec - 1));
+        }
+    };
+    static_assert(kShortCap <= kR * E::kPerVec, "one round covers a row that keeps every score");
+    uint32_t T = 0u;
+    if (keep_all) load(0, xa);
+    else T = short_cutoff<E>(row, L, m, reinterpret_cast<uint32_t*>(buf), lds, first_loads);
+    B::sync();  // the sample's keys are read; the buffer takes survivors now
+
     auto filter = [&](const Vec (&x)[kU], int64_t base) {
         uint32_t cnt = 0u;
 #pragma unroll
@@ -458,11 +494,9 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
             }
         }
     };
-    Vec xa[kU], xc[kU];
     int64_t base = 0;
-    if (base < nvec) load(base, xa);
     while (base < nvec) {  // uniform over the workgroup
-        if (base + kR < nvec) load(base + kR, xc);
+        if (base > 0 && base + kR < nvec) load(base + kR, xc);  // round 1 is in flight already
         filter(xa, base);
         base += kR;
         if (base >= nvec) break;

@@ -79,7 +79,7 @@ int oracle_max_threads(void) {
  * k           slots per row, >= 1
  * page_table  [batch, page_table_stride] int32, or NULL for raw indices
  * out         [batch, k] int32, written completely
- * threads     OpenMP threads over rows (0: the runtime default)
+ * threads     OpenMP threads over rows for this call (0: the runtime default)
  * Rows are independent; the parallel loop only splits rows over threads.
  */
 int oracle_topk(const float* scores, int64_t batch, int64_t row_stride,
@@ -91,12 +91,13 @@ int oracle_topk(const float* scores, int64_t batch, int64_t row_stride,
     if (page_table != NULL && page_size < 1) return ORACLE_ERR_ARG;
     int status = ORACLE_OK;
 #ifdef _OPENMP
-    if (threads > 0) omp_set_num_threads(threads);
+    /* a clause, not omp_set_num_threads: a later call with 0 gets the default again */
+    const int nt = threads > 0 ? threads : omp_get_max_threads();
 #else
     (void)threads;
 #endif
 
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
     for (int64_t b = 0; b < batch; ++b) {
         int64_t L = lengths ? (int64_t)lengths[b] : n_cols;
         if (L < 0) L = 0;

@@ -135,6 +135,8 @@ struct F32Elem {
     static constexpr int kUnroll = 8;  // loads per lane per round: 32 scores
     __device__ static uint32_t bits(const Vec& v, int j) { return __float_as_uint(v[j]); }
     __device__ static uint32_t scalar_bits(Scalar x) { return __float_as_uint(x); }
+    static constexpr int kKeyShift = 0;  // every key bit carries information
+    __device__ static uint32_t full_key(uint32_t v) { return v; }
 };
 struct Bf16Elem {
     typedef u4 Vec;
@@ -145,6 +147,11 @@ struct Bf16Elem {
         return (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
     }
     __device__ static uint32_t scalar_bits(Scalar x) { return (uint32_t)x << 16; }
+    // The order key of a widened bf16 score is fixed by its top 16 bits: the
+    // low 16 are 0 for a non-negative score (key bit 31 set) and all ones for
+    // a negative one, so selecting on key >> 16 is exact.
+    static constexpr int kKeyShift = 16;
+    __device__ static uint32_t full_key(uint32_t v) { return (v << 16) | ((v >> 15) & 1u ? 0u : 0xFFFFu); }
 };
 
 template <class E>
@@ -397,6 +404,51 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
 // short rows: one workgroup per row, survivors in LDS, one launch
 // ----------------------------------------------------------------------------
 
+// Exact top m of a short row's survivors (keys >= T), ties at the cutoff to
+// the lowest positions, as select_top does, with two savings: keys are
+// selected on key >> E::kKeyShift, which drops only bits that carry no
+// information (bf16: 2 digit passes where 32-bit keys take 3), and when at
+// most 64 survivors equal the cutoff key their positions are gathered and
+// ranked by one wave instead of by radix passes over the positions.
+// `ties` is 66 words of LDS, ties[64] zero on entry.
+template <class E>
+__device__ Selection short_select(SelectLds lds, const PairSource<BlockScope<kThreads>>& src, uint32_t m,
+                                  uint32_t n, uint32_t T, int idx_bits, uint32_t* ties) {
+    using B = BlockScope<kThreads>;
+    constexpr int kShift = E::kKeyShift;
+    const uint32_t lo = T >> kShift, hi = 0xFFFFFFFFu >> kShift;
+    const int nbits = lo == hi ? 0 : 32 - __clz(lo ^ hi);
+    const Cut c = radix_select<B>(lds, src, CoarseKeyView<kShift>{}, m, lo, nbits, n);
+    if (c.range) return at_least(c.value << kShift);  // the least full key whose top bits reach c.value
+    const uint32_t kth = E::full_key(c.value);
+    Selection sel{kth, INT32_MAX};
+    if (c.need >= c.equal) return sel;
+    if (c.equal <= 64u) {
+        // exactly c.equal survivors have the cutoff key
+        src.for_each([&](uint32_t key, uint32_t idx) {
+            if (key == kth) ties[atomicAdd(&ties[64], 1u)] = idx;
+        });
+        B::sync();
+        if (B::first_wave()) {
+            // positions are distinct: the lane whose position has need - 1
+            // smaller ones holds the cutoff position
+            const uint32_t lane = lane_id();
+            const uint32_t v = lane < c.equal ? ties[lane] : 0xFFFFFFFFu;
+            uint32_t below = 0u;
+            for (uint32_t j = 0; j < c.equal; ++j) below += __shfl(v, (int)j) < v ? 1u : 0u;
+            if (lane < c.equal && below == c.need - 1u) ties[65] = v;
+        }
+        B::sync();
+        sel.icut = (int32_t)ties[65];
+        return sel;
+    }
+    // the need-th largest inverted index among the ties (select_top's way)
+    const uint32_t iprefix = idx_bits >= 32 ? 0u : (0xFFFFFFFFu << idx_bits);
+    const Cut t = radix_select<B>(lds, src, TieIndexView{kth}, c.need, iprefix, idx_bits, c.equal);
+    sel.icut = (int32_t)(~t.value);
+    return sel;
+}
+
 // Survivor entries a short-row workgroup holds in LDS. Rows of at most
 // kShortMaxCols scores with k <= 2048 keep about 2900 survivors at most on
 // average (the sample's rank rule), so overflow needs a row far from its
@@ -414,6 +466,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     __shared__ uint32_t found[3];
     __shared__ uint32_t count;
     __shared__ uint32_t emitted;
+    __shared__ uint32_t ties[66];  // tied positions, their count, the cutoff position
     static_assert(kShortCap * 2 >= kMaxSample, "the sample fits the survivor buffer");
     const int64_t b = blockIdx.x;
     const int64_t L = split_row_len(p, b);
@@ -428,6 +481,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     if (threadIdx.x == 0) {
         count = 0u;
         emitted = 0u;
+        ties[64] = 0u;
     }
     B::sync();
     const SelectLds lds{hist, found};
@@ -523,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     } else {
         code = keep_all ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
         const PairSource<B> src{buf, n};
-        const Selection s = select_top<B>(lds, src, m, n, T, 0xFFFFFFFFu, bits_for(L));
+        const Selection s = short_select<E>(lds, src, m, n, T, bits_for(L), ties);
         emit(src, s, out);
     }
     if (threadIdx.x == 0) split_stats(p, b, code, n);

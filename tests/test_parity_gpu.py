@@ -459,6 +459,51 @@ def test_bf16_page_sizes(topk, page_size):
     assert not fails, "\n".join(fails)
 
 
+def tie_rows(ties, W=16384, k=512, seed=41):
+    """bf16 bit patterns of 4 rows whose cutoff falls inside a group of `ties`
+    equal scores: k - 17 distinct scores above it (consecutive bf16 patterns),
+    the rest below. Rows 0 and 2 tie at +32, rows 1 and 3 at -1 (the order key
+    of a negative bf16 score has its low 16 bits set); rows 2 and 3 are
+    ragged."""
+    rng = np.random.default_rng(seed + ties)
+    above = k - 17
+    bits = np.empty((4, W), np.uint16)
+    for b in range(4):
+        if b % 2 == 0:   # background |N(0,1)| < 32, ties at +32, above from +64 up
+            row = synth.to_bf16_bits(rng.standard_normal(W).astype(np.float32))
+            tie, top = 0x4200, 0x4280 + np.arange(above)
+        else:            # background below -2, ties at -1, above from +1 up
+            row = synth.to_bf16_bits((-2.0 - np.abs(rng.standard_normal(W))).astype(np.float32))
+            tie, top = 0xBF80, 0x3F80 + np.arange(above)
+        pos = rng.permutation(W - 8)[:above + ties]
+        row[pos[:above]] = top
+        row[pos[above:]] = tie
+        bits[b] = row
+    lengths = np.array([W, W, W - 5, W - 7], np.int32)
+    return bits, lengths
+
+
+@pytest.mark.parametrize("ties", [18, 63, 64, 65, 300])
+def test_short_rows_ties_at_the_cutoff(topk, ties):
+    # 17 of the tied scores are taken, those at the lowest positions: up to 64
+    # tied positions are ranked by one wave, more by radix passes; the same
+    # rows as fp32 and as bf16
+    W, k = 16384, 512
+    bits, lengths = tie_rows(ties, W, k)
+    synth.poison_tails_bf16(bits, lengths)
+    scores = oracle.bf16_to_f32(bits)
+    wl = synth.Workload(f"ties{ties}", 41, scores, lengths, W, k)
+    got, _ = run(topk, wl)
+    assert_parity(wl, got, expect(wl))
+    s = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    say(f"  gpu bf16 call: ties{ties}")
+    out = topk.topk_select_bf16(s, torch.from_numpy(lengths).cuda(), k)
+    torch.cuda.synchronize()
+    want = oracle.topk_bf16(bits, lengths, k)
+    fails = check(scores, lengths, W, k, out.cpu().numpy(), want)
+    assert not fails, "\n".join(fails)
+
+
 # ----------------------------------------------------------------------------
 # a sample that sees only the peaks: survivors fall short of m
 # ----------------------------------------------------------------------------

@@ -404,22 +404,46 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
 // short rows: one workgroup per row, survivors in LDS, one launch
 // ----------------------------------------------------------------------------
 
-// Exact top m of a short row's survivors (keys >= T), ties at the cutoff to
-// the lowest positions, as select_top does, with two savings: keys are
-// selected on key >> E::kKeyShift, which drops only bits that carry no
-// information (bf16: 2 digit passes where 32-bit keys take 3), and when at
-// most 64 survivors equal the cutoff key their positions are gathered and
-// ranked by one wave instead of by radix passes over the positions.
-// `ties` is 66 words of LDS, ties[64] zero on entry.
+// The first pass of a short row's selection: the bin of (key >> shift -
+// base) >> sh, with base aligned to 2^sh, so that bin d holds exactly the
+// keys whose top bits are (base >> sh) + d.
+template <int kShift>
+struct AboveBinView {
+    uint32_t base;
+    int sh;
+    __device__ bool operator()(uint32_t key, uint32_t, uint32_t& v) const {
+        v = ((key >> kShift) - base) >> sh;
+        return true;
+    }
+};
+
+// Exact top m of a short row's survivors (keys in [T, vmax]), ties at the
+// cutoff to the lowest positions, as select_top does, with three savings.
+// Keys are selected on key >> E::kKeyShift, which drops only bits that carry
+// no information (bf16: 16-bit keys). The first pass bins [T, vmax] into at
+// most 2047 bins of equal width (a power of two), so the survivors spread
+// over many bins instead of the few that their top 11 bits share; bins of
+// width 1 settle the cutoff in that pass. And when at most 64 survivors equal
+// the cutoff key, their positions are gathered and ranked by one wave
+// instead of by radix passes over the positions. `ties` is 66 words of LDS,
+// ties[64] zero on entry.
 template <class E>
 __device__ Selection short_select(SelectLds lds, const PairSource<BlockScope<kThreads>>& src, uint32_t m,
-                                  uint32_t n, uint32_t T, int idx_bits, uint32_t* ties) {
+                                  uint32_t n, uint32_t T, uint32_t vmax, int idx_bits, uint32_t* ties) {
     using B = BlockScope<kThreads>;
     constexpr int kShift = E::kKeyShift;
-    const uint32_t lo = T >> kShift, hi = 0xFFFFFFFFu >> kShift;
-    const int nbits = lo == hi ? 0 : 32 - __clz(lo ^ hi);
-    const Cut c = radix_select<B>(lds, src, CoarseKeyView<kShift>{}, m, lo, nbits, n);
-    if (c.range) return at_least(c.value << kShift);  // the least full key whose top bits reach c.value
+    const uint32_t lo = T >> kShift, hi = vmax >> kShift;  // every survivor's value lies in [lo, hi]
+    int sh = 0;
+    while (((hi - lo) >> sh) >= (uint32_t)(kBins - 1)) ++sh;
+    const uint32_t base = sh >= 32 ? 0u : lo & ~((1u << sh) - 1u);  // (hi - base) >> sh < kBins
+    const Cut c1 = radix_select<B>(lds, src, AboveBinView<kShift>{base, sh}, m, 0u, kDigitBits, n);
+    const uint32_t edge = base + (c1.value << sh);  // lowest value in the cutoff bin
+    if (c1.need == c1.equal) return at_least(edge << kShift);  // the bin is taken whole
+    Cut c{edge, c1.need, c1.equal, false};
+    if (sh > 0) {
+        c = radix_select<B>(lds, src, CoarseKeyView<kShift>{}, c1.need, edge, sh, c1.equal);
+        if (c.range) return at_least(c.value << kShift);  // the least full key whose top bits reach c.value
+    }
     const uint32_t kth = E::full_key(c.value);
     Selection sel{kth, INT32_MAX};
     if (c.need >= c.equal) return sel;
@@ -467,6 +491,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     __shared__ uint32_t count;
     __shared__ uint32_t emitted;
     __shared__ uint32_t ties[66];  // tied positions, their count, the cutoff position
+    __shared__ uint32_t smax;      // the largest survivor key
     static_assert(kShortCap * 2 >= kMaxSample, "the sample fits the survivor buffer");
     const int64_t b = blockIdx.x;
     const int64_t L = split_row_len(p, b);
@@ -482,6 +507,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         count = 0u;
         emitted = 0u;
         ties[64] = 0u;
+        smax = 0u;
     }
     B::sync();
     const SelectLds lds{hist, found};
@@ -524,6 +550,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     else T = short_cutoff<E>(row, L, m, reinterpret_cast<uint32_t*>(buf), lds, first_loads);
     B::sync();  // the sample's keys are read; the buffer takes survivors now
 
+    uint32_t hmax = 0u;  // this lane's largest survivor key
     auto filter = [&](const Vec (&x)[kU], int64_t base) {
         uint32_t cnt = 0u;
 #pragma unroll
@@ -540,9 +567,11 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
 #pragma unroll
                 for (int j = 0; j < E::kPerVec; ++j) {
                     const uint32_t bits = E::bits(x[u], j);
-                    if (g < nvec && elem_key<E>(bits) >= T) {
+                    const uint32_t key = elem_key<E>(bits);
+                    if (g < nvec && key >= T) {
                         if (slot < (uint32_t)kShortCap) buf[slot] = make_uint2(bits, (uint32_t)(E::kPerVec * g + j));
                         ++slot;
+                        hmax = max(hmax, key);
                     }
                 }
             }
@@ -564,7 +593,10 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         const bool hit = i < L && elem_key<E>(bits) >= T;
         const uint32_t slot = wave_reserve_count(&count, hit ? 1u : 0u);
         if (hit && slot < (uint32_t)kShortCap) buf[slot] = make_uint2(bits, (uint32_t)i);
+        if (hit) hmax = max(hmax, elem_key<E>(bits));
     }
+    hmax = wave_max(hmax);
+    if (lane_id() == 0) atomicMax(&smax, hmax);
     B::sync();
     const uint32_t n = count;
     OutRow out = split_out_row(p, b, m, &emitted);
@@ -577,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     } else {
         code = keep_all ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
         const PairSource<B> src{buf, n};
-        const Selection s = short_select<E>(lds, src, m, n, T, bits_for(L), ties);
+        const Selection s = short_select<E>(lds, src, m, n, T, smax, bits_for(L), ties);
         emit(src, s, out);
     }
     if (threadIdx.x == 0) split_stats(p, b, code, n);

@@ -348,63 +348,7 @@ __global__ __launch_bounds__(kThreads) void split_stream_kernel(SplitParams p) {
     stream_piece(p, b, split_row_len(p, b), h->T, piece, h, p.surv + b * kSplitCapacity, (uint32_t)p.capacity);
 }
 
-// launch 3: the exact top m of each row
-__global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p) {
-    using B = BlockScope<kFinThreads>;
-    __shared__ uint2 lsurv[kSplitCapacity];
-    __shared__ uint32_t hist[kBins];
-    __shared__ uint32_t found[3];
-    __shared__ uint32_t emitted;
-    const int64_t b = blockIdx.x;
-    const SplitHead head = p.head[b];
-    if (head.kind == kKindDirect) return;
-    for (int i = (int)threadIdx.x; i < kBins; i += kFinThreads) hist[i] = 0u;
-    if (threadIdx.x == 0) emitted = 0u;
-    const int64_t L = split_row_len(p, b);
-    const uint32_t m = (uint32_t)(L < p.k ? L : p.k);
-    const uint32_t n = head.count;
-    const uint32_t cap = (uint32_t)p.capacity;
-    const SelectLds lds{hist, found};
-    OutRow out = split_out_row(p, b, m, &emitted);
-    int code;
-    if (head.kind == kKindFull || n > cap || n < m) {
-        code = head.kind == kKindFull ? TOPK_ROW_FULL_FORCED : (n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW);
-        B::sync();
-        const RowSource<B> src{p.scores + b * p.row_stride, L};
-        const Selection s = select_top<B>(lds, src, m, (uint32_t)L, 0u, 0xFFFFFFFFu, bits_for(L));
-        emit(src, s, out);
-    } else {
-        code = head.kind == kKindAll ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
-        // survivors in 16-byte pairs; an odd count reads one unused entry
-        // past it, still inside the row's area (n < capacity <= area)
-        constexpr int kPer = (int)(kSplitCapacity / 2 / kFinThreads);
-        const uint4* g4 = reinterpret_cast<const uint4*>(p.surv + b * kSplitCapacity);
-        uint4* l4 = reinterpret_cast<uint4*>(lsurv);
-        const uint32_t npair = (n + 1u) / 2u;
-        uint4 v[kPer];
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const uint32_t i = (uint32_t)(q * kFinThreads) + threadIdx.x;
-            v[q] = i < npair ? g4[i] : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const uint32_t i = (uint32_t)(q * kFinThreads) + threadIdx.x;
-            if (i < npair) l4[i] = v[q];
-        }
-        B::sync();
-        const PairSource<B> src{lsurv, n};
-        const Selection s = select_top<B>(lds, src, m, n, head.T, 0xFFFFFFFFu, bits_for(L));
-        emit(src, s, out);
-    }
-    if (threadIdx.x == 0) split_stats(p, b, code, head.kind == kKindFull ? (uint32_t)L : n);
-}
-
-// ----------------------------------------------------------------------------
-// short rows: one workgroup per row, survivors in LDS, one launch
-// ----------------------------------------------------------------------------
-
-// The first pass of a short row's selection: the bin of (key >> shift -
+// The first pass of a survivor selection: the bin of (key >> shift -
 // base) >> sh, with base aligned to 2^sh, so that bin d holds exactly the
 // keys whose top bits are (base >> sh) + d.
 template <int kShift>
@@ -417,7 +361,8 @@ struct AboveBinView {
     }
 };
 
-// Exact top m of a short row's survivors (keys in [T, vmax]), ties at the
+// Exact top m of a row's survivors held in LDS by workgroup scope B (keys in
+// [T, vmax]; the short-row and split-finish kernels), ties at the
 // cutoff to the lowest positions, as select_top does, with three savings.
 // Keys are selected on key >> E::kKeyShift, which drops only bits that carry
 // no information (bf16: 16-bit keys). The first pass bins [T, vmax] into at
@@ -427,10 +372,9 @@ struct AboveBinView {
 // the cutoff key, their positions are gathered and ranked by one wave
 // instead of by radix passes over the positions. `ties` is 66 words of LDS,
 // ties[64] zero on entry.
-template <class E>
-__device__ Selection short_select(SelectLds lds, const PairSource<BlockScope<kThreads>>& src, uint32_t m,
-                                  uint32_t n, uint32_t T, uint32_t vmax, int idx_bits, uint32_t* ties) {
-    using B = BlockScope<kThreads>;
+template <class E, class B>
+__device__ Selection short_select(SelectLds lds, const PairSource<B>& src, uint32_t m, uint32_t n, uint32_t T,
+                                  uint32_t vmax, int idx_bits, uint32_t* ties) {
     constexpr int kShift = E::kKeyShift;
     const uint32_t lo = T >> kShift, hi = vmax >> kShift;  // every survivor's value lies in [lo, hi]
     int sh = 0;
@@ -472,6 +416,75 @@ __device__ Selection short_select(SelectLds lds, const PairSource<BlockScope<kTh
     sel.icut = (int32_t)(~t.value);
     return sel;
 }
+
+// launch 3: the exact top m of each row
+__global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p) {
+    using B = BlockScope<kFinThreads>;
+    __shared__ uint2 lsurv[kSplitCapacity];
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t found[3];
+    __shared__ uint32_t emitted;
+    __shared__ uint32_t ties[66];  // tied positions, their count, the cutoff position
+    __shared__ uint32_t smax;      // the largest survivor key
+    const int64_t b = blockIdx.x;
+    const SplitHead head = p.head[b];
+    if (head.kind == kKindDirect) return;
+    for (int i = (int)threadIdx.x; i < kBins; i += kFinThreads) hist[i] = 0u;
+    if (threadIdx.x == 0) {
+        emitted = 0u;
+        ties[64] = 0u;
+        smax = 0u;
+    }
+    const int64_t L = split_row_len(p, b);
+    const uint32_t m = (uint32_t)(L < p.k ? L : p.k);
+    const uint32_t n = head.count;
+    const uint32_t cap = (uint32_t)p.capacity;
+    const SelectLds lds{hist, found};
+    OutRow out = split_out_row(p, b, m, &emitted);
+    int code;
+    if (head.kind == kKindFull || n > cap || n < m) {
+        code = head.kind == kKindFull ? TOPK_ROW_FULL_FORCED : (n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW);
+        B::sync();
+        const RowSource<B> src{p.scores + b * p.row_stride, L};
+        const Selection s = select_top<B>(lds, src, m, (uint32_t)L, 0u, 0xFFFFFFFFu, bits_for(L));
+        emit(src, s, out);
+    } else {
+        code = head.kind == kKindAll ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
+        // survivors in 16-byte pairs; an odd count reads one unused entry
+        // past it, still inside the row's area (n < capacity <= area)
+        constexpr int kPer = (int)(kSplitCapacity / 2 / kFinThreads);
+        const uint4* g4 = reinterpret_cast<const uint4*>(p.surv + b * kSplitCapacity);
+        uint4* l4 = reinterpret_cast<uint4*>(lsurv);
+        const uint32_t npair = (n + 1u) / 2u;
+        uint4 v[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const uint32_t i = (uint32_t)(q * kFinThreads) + threadIdx.x;
+            v[q] = i < npair ? g4[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        uint32_t hmax = 0u;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const uint32_t i = (uint32_t)(q * kFinThreads) + threadIdx.x;
+            if (i < npair) {
+                l4[i] = v[q];
+                hmax = max(hmax, order_key(__uint_as_float(v[q].x)));
+                if (2u * i + 1u < n) hmax = max(hmax, order_key(__uint_as_float(v[q].z)));
+            }
+        }
+        hmax = wave_max(hmax);
+        if (lane_id() == 0) atomicMax(&smax, hmax);
+        B::sync();
+        const PairSource<B> src{lsurv, n};
+        const Selection s = short_select<F32Elem, B>(lds, src, m, n, head.T, smax, bits_for(L), ties);
+        emit(src, s, out);
+    }
+    if (threadIdx.x == 0) split_stats(p, b, code, head.kind == kKindFull ? (uint32_t)L : n);
+}
+
+// ----------------------------------------------------------------------------
+// short rows: one workgroup per row, survivors in LDS, one launch
+// ----------------------------------------------------------------------------
 
 // Survivor entries a short-row workgroup holds in LDS. Rows of at most
 // kShortMaxCols scores with k <= 2048 keep about 2900 survivors at most on
@@ -609,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     } else {
         code = keep_all ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
         const PairSource<B> src{buf, n};
-        const Selection s = short_select<E>(lds, src, m, n, T, smax, bits_for(L), ties);
+        const Selection s = short_select<E, B>(lds, src, m, n, T, smax, bits_for(L), ties);
         emit(src, s, out);
     }
     if (threadIdx.x == 0) split_stats(p, b, code, n);

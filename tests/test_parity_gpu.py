@@ -504,6 +504,34 @@ def test_short_rows_ties_at_the_cutoff(topk, ties):
     assert not fails, "\n".join(fails)
 
 
+@pytest.mark.parametrize("n_inf,k", [(1, 512), (100, 512), (512, 512), (600, 512), (50, 40), (5000, 512)])
+def test_short_rows_infinities(topk, n_inf, k):
+    # +inf keys share the selection's top bin: a finite cutoff (1, 100), the
+    # top bin taken whole (512), ties at +inf by radix passes (600) or by one
+    # wave (50 of k = 40), and more than the buffer holds (5000); as fp32 and
+    # as bf16 rows, the last row +inf at its last valid position only
+    W = 16384
+    rng = np.random.default_rng(42 + n_inf)
+    x = (rng.standard_normal((4, W)) + 1.4).astype(np.float32)
+    lengths = np.array([W, W - 3, 9000, 12001], np.int32)
+    for b in range(3):
+        x[b, rng.permutation(int(lengths[b]))[:n_inf]] = np.inf
+    x[3, lengths[3] - 1] = np.inf
+    bits = synth.to_bf16_bits(x)
+    synth.poison_tails_bf16(bits, lengths)
+    scores = oracle.bf16_to_f32(bits)
+    wl = synth.Workload(f"inf{n_inf}", 42, scores, lengths, W, k)
+    got, _ = run(topk, wl)
+    assert_parity(wl, got, expect(wl))
+    s = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    say(f"  gpu bf16 call: inf{n_inf} k={k}")
+    out = topk.topk_select_bf16(s, torch.from_numpy(lengths).cuda(), k)
+    torch.cuda.synchronize()
+    want = oracle.topk_bf16(bits, lengths, k)
+    fails = check(scores, lengths, W, k, out.cpu().numpy(), want)
+    assert not fails, "\n".join(fails)
+
+
 # ----------------------------------------------------------------------------
 # a sample that sees only the peaks: survivors fall short of m
 # ----------------------------------------------------------------------------

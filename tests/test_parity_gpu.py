@@ -506,10 +506,11 @@ def test_short_rows_ties_at_the_cutoff(topk, ties):
 
 @pytest.mark.parametrize("n_inf,k", [(1, 512), (100, 512), (512, 512), (600, 512), (50, 40), (5000, 512)])
 def test_short_rows_infinities(topk, n_inf, k):
-    # +inf keys share the selection's top bin: a finite cutoff (1, 100), the
-    # top bin taken whole (512), ties at +inf by radix passes (600) or by one
-    # wave (50 of k = 40), and more than the buffer holds (5000); as fp32 and
-    # as bf16 rows, the last row +inf at its last valid position only
+    # +inf scores in a short row: a finite cutoff (1, 100), every +inf taken
+    # exactly (512), ties at +inf ranked by radix passes (600) or by one wave
+    # (50 of k = 40), and more survivors than the buffer holds (5000); as
+    # fp32 and as bf16 rows, the last row +inf at its last valid position only
+    # (the block-max kernel's newest block)
     W = 16384
     rng = np.random.default_rng(42 + n_inf)
     x = (rng.standard_normal((4, W)) + 1.4).astype(np.float32)

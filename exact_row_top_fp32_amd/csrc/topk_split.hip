@@ -189,6 +189,19 @@ struct ElemRowSource {
 // `issue` runs right after the sample's loads are issued (and on the early
 // return), so that a caller's own loads are in flight while the cutoff is
 // found.
+constexpr uint32_t kInfKey = 0xFF800000u;  // order key of +inf
+
+// A sample key at or above lo: keys up to hi binned (key - base) >> sh,
+// keys above hi (+inf) in the top bin.
+struct SampleBinView {
+    uint32_t lo, hi, base;
+    int sh;
+    __device__ bool operator()(uint32_t key, uint32_t, uint32_t& v) const {
+        v = key > hi ? (uint32_t)(kBins - 1) : (key - base) >> sh;
+        return key >= lo;
+    }
+};
+
 struct NoIssue {
     __device__ void operator()() const {}
 };
@@ -218,22 +231,70 @@ __device__ uint32_t short_cutoff(const typename E::Scalar* row, int64_t L, uint3
         if (t < nsv) x[h] = rv[start + t % kVecPerRun];
     }
     issue();
+    const uint32_t n = (uint32_t)(E::kPerVec * nsv);
+    const float mu = (float)m * (float)n / (float)L;
+    const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
+    const uint32_t want = wantf < (float)n ? (uint32_t)wantf : 0u;  // 0: keep every score
+    // Each lane also keeps its kQ largest keys (and so its largest). With
+    // q = ceil(want / kThreads) <= kQ, the smallest of the lanes' q-th
+    // largest keys, lo, has at least want keys at or above it (a lane with
+    // fewer than q keys gives lo = 0).
+    constexpr int kQ = 4;
+    uint32_t top[kQ] = {0u, 0u, 0u, 0u};
+    uint32_t fin = 0u;  // the lane's largest key below +inf's
 #pragma unroll
     for (int h = 0; h < kPer; ++h) {
         const int t = h * kThreads + (int)threadIdx.x;
         if (t < nsv) {
 #pragma unroll
-            for (int j = 0; j < E::kPerVec; ++j) skey[E::kPerVec * t + j] = elem_key<E>(E::bits(x[h], j));
+            for (int j = 0; j < E::kPerVec; ++j) {
+                uint32_t key = elem_key<E>(E::bits(x[h], j));
+                skey[E::kPerVec * t + j] = key;
+                fin = max(fin, key < kInfKey ? key : 0u);
+#pragma unroll
+                for (int i = 0; i < kQ; ++i) {
+                    const uint32_t hi = max(top[i], key);
+                    key = min(top[i], key);
+                    top[i] = hi;
+                }
+            }
+        }
+    }
+    const uint32_t q = (want + kThreads - 1) / kThreads;
+    const bool one_pass = want > 0u && q <= (uint32_t)kQ;  // uniform
+    __shared__ uint32_t s_lo, s_hi;
+    if (one_pass) {
+        if (threadIdx.x == 0) {
+            s_lo = 0xFFFFFFFFu;
+            s_hi = 0u;
+        }
+        B::sync();
+        uint32_t lane_lo = top[0];
+#pragma unroll
+        for (int i = 1; i < kQ; ++i) lane_lo = (uint32_t)(i + 1) == q ? top[i] : lane_lo;
+        const uint32_t wlo = wave_min(lane_lo), whi = wave_max(fin);
+        if (lane_id() == 0) {
+            atomicMin(&s_lo, wlo);
+            atomicMax(&s_hi, whi);
         }
     }
     B::sync();
-    const uint32_t n = (uint32_t)(E::kPerVec * nsv);
-    const float mu = (float)m * (float)n / (float)L;
-    const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
-    if (wantf >= (float)n) return 0u;
+    if (want == 0u) return 0u;
+    if (one_pass) {
+        // one histogram of the keys in [lo, hi] (hi the largest below +inf),
+        // in at most kBins - 1 bins of width 2^sh from a base aligned to it,
+        // keys above hi in the top bin: T is the lower edge of the bin holding
+        // the want-th largest key, or hi + 1 when that key is above hi (bf16
+        // keys differ by at least 2^16, so their bins hold one value each)
+        const uint32_t lo = s_lo, hi = max(s_hi, lo);
+        int sh = 0;
+        while (((hi - lo) >> sh) >= (uint32_t)(kBins - 2)) ++sh;
+        const uint32_t base = lo & ~((1u << sh) - 1u);  // (hi - base) >> sh <= kBins - 2
+        const Cut c = radix_select<B>(lds, LdsKeys{skey, n}, SampleBinView{lo, hi, base, sh}, want, 0u, kDigitBits, n);
+        return c.value == (uint32_t)(kBins - 1) ? hi + 1u : base + (c.value << sh);
+    }
     constexpr int kDropBits = 32 - 2 * kDigitBits;
-    return radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, (uint32_t)wantf, 0u, 2 * kDigitBits, n)
-               .value
+    return radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, want, 0u, 2 * kDigitBits, n).value
            << kDropBits;
 }
 

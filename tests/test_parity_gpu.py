@@ -318,6 +318,29 @@ def test_negative_and_straddling_cutoffs(topk, k):
         assert np.all(stats[:8, 0] == 3), stats[:8]
 
 
+@pytest.mark.parametrize("k", [512, 2048])
+def test_short_rows_straddling_cutoffs(topk, k):
+    # Short rows shifted so the cutoff falls below +0 (every score negative)
+    # or near it (k = 2048: about 12.5 % positive at shift 1.15; k = 512:
+    # about 3 % at 1.86): the sample's keys then straddle the sign, the
+    # cutoff's first histogram is coarse and a second pass narrows it. Every
+    # row must still take the sampled path (no overflow into the full row).
+    rng = np.random.default_rng(33)
+    B, W = 24, 16384
+    shift = np.empty((B, 1), np.float32)
+    shift[:8] = 10.0
+    shift[8:16] = 1.15
+    shift[16:] = 1.86
+    scores = (rng.standard_normal((B, W)).astype(np.float32) - shift).astype(np.float32)
+    lengths = synth.ragged_lengths(rng, B, W)
+    synth.poison_tails(scores, lengths)
+    wl = synth.Workload("short_negative_cutoffs", 33, scores, lengths, W, k)
+    got, stats = run(topk, wl, want_stats=True)
+    assert_parity(wl, got, expect(wl))
+    say("  row paths:", dict(zip(*np.unique(stats[:, 0], return_counts=True))))
+    assert np.all(stats[:, 0] == 3), stats[:, 0]
+
+
 def test_batch_above_longest_first_table(topk):
     # 3000 rows of 8192 (above the LDS capacity): rows are claimed in batch
     # order once the batch no longer fits the longest-first table.

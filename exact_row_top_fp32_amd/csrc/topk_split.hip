@@ -177,18 +177,6 @@ struct ElemRowSource {
     }
 };
 
-// The cutoff key of a row from its sample: `runs` runs of 64 contiguous
-// scores at evenly spaced offsets over [0, L). When the sample has fewer than
-// `want` keys above the row's m-th largest, fewer than m scores can be at or
-// above T; the rank is set so that this is a six-sigma event: the number of
-// sample keys at or above the m-th largest score is binomial with mean
-// mu = m n / L, and want = ceil(mu + 6 sqrt(mu) + 4). T is the lowest key of
-// the want-th largest sample key's top 22 bits (two 11-bit digits), so at
-// most that key and at most 2^10 keys (1/8192 of a binade) below it.
-//
-// `issue` runs right after the sample's loads are issued (and on the early
-// return), so that a caller's own loads are in flight while the cutoff is
-// found.
 constexpr uint32_t kInfKey = 0xFF800000u;  // order key of +inf
 
 // A sample key at or above lo: keys up to hi binned (key - base) >> sh,
@@ -202,6 +190,21 @@ struct SampleBinView {
     }
 };
 
+// The cutoff key of a row from its sample: `runs` runs of 64 contiguous
+// scores at evenly spaced offsets over [0, L). When the sample has fewer than
+// `want` keys above the row's m-th largest, fewer than m scores can be at or
+// above T; the rank is set so that this is a six-sigma event: the number of
+// sample keys at or above the m-th largest score is binomial with mean
+// mu = m n / L, and want = ceil(mu + 6 sqrt(mu) + 4). T is at or below the
+// want-th largest sample key: the lower edge of its bin in one histogram of
+// the keys in [lo, hi] (lo a bound from each lane's largest keys, hi the
+// largest below +inf's, bins a power of two wide), or, when the lanes hold
+// too few keys for that bound, the lowest key of its top 22 bits (two 11-bit
+// digits, at most 2^10 keys below it).
+//
+// `issue` runs right after the sample's loads are issued (and on the early
+// return), so that a caller's own loads are in flight while the cutoff is
+// found.
 struct NoIssue {
     __device__ void operator()() const {}
 };

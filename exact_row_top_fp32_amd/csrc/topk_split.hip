@@ -209,15 +209,20 @@ struct NoIssue {
     __device__ void operator()() const {}
 };
 
+struct Cutoff {
+    uint32_t T;   // the cutoff key
+    uint32_t hi;  // the sample's largest key below +inf's (0xFFFFFFFF: no sample)
+};
+
 template <class E, class Issue = NoIssue>
-__device__ uint32_t short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, uint32_t* skey,
-                                 SelectLds lds, Issue&& issue = Issue{}) {
+__device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, uint32_t* skey,
+                               SelectLds lds, Issue&& issue = Issue{}) {
     using B = BlockScope<kThreads>;
     const int64_t fit = L / (2 * kRunLen);
     const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
     if (runs < 2) {
         issue();
-        return 0u;
+        return Cutoff{0u, 0xFFFFFFFFu};
     }
     constexpr int kVecPerRun = kRunLen / E::kPerVec;
     constexpr int kPer = kMaxSample / E::kPerVec / kThreads;  // loads per lane, all in flight
@@ -266,39 +271,40 @@ __device__ uint32_t short_cutoff(const typename E::Scalar* row, int64_t L, uint3
     const uint32_t q = (want + kThreads - 1) / kThreads;
     const bool one_pass = want > 0u && q <= (uint32_t)kQ;  // uniform
     __shared__ uint32_t s_lo, s_hi;
-    if (one_pass) {
-        if (threadIdx.x == 0) {
-            s_lo = 0xFFFFFFFFu;
-            s_hi = 0u;
-        }
-        B::sync();
-        uint32_t lane_lo = top[0];
-#pragma unroll
-        for (int i = 1; i < kQ; ++i) lane_lo = (uint32_t)(i + 1) == q ? top[i] : lane_lo;
-        const uint32_t wlo = wave_min(lane_lo), whi = wave_max(fin);
-        if (lane_id() == 0) {
-            atomicMin(&s_lo, wlo);
-            atomicMax(&s_hi, whi);
-        }
+    if (threadIdx.x == 0) {
+        s_lo = 0xFFFFFFFFu;
+        s_hi = 0u;
     }
     B::sync();
-    if (want == 0u) return 0u;
+    uint32_t lane_lo = top[0];
+#pragma unroll
+    for (int i = 1; i < kQ; ++i) lane_lo = (uint32_t)(i + 1) == q ? top[i] : lane_lo;
+    const uint32_t wlo = wave_min(lane_lo), whi = wave_max(fin);
+    if (lane_id() == 0) {
+        atomicMin(&s_lo, wlo);
+        atomicMax(&s_hi, whi);
+    }
+    B::sync();
+    const uint32_t shi = s_hi;
+    if (want == 0u) return Cutoff{0u, shi};
     if (one_pass) {
         // one histogram of the keys in [lo, hi] (hi the largest below +inf),
         // in at most kBins - 1 bins of width 2^sh from a base aligned to it,
         // keys above hi in the top bin: T is the lower edge of the bin holding
         // the want-th largest key, or hi + 1 when that key is above hi (bf16
         // keys differ by at least 2^16, so their bins hold one value each)
-        const uint32_t lo = s_lo, hi = max(s_hi, lo);
+        const uint32_t lo = s_lo, hi = max(shi, lo);
         int sh = 0;
         while (((hi - lo) >> sh) >= (uint32_t)(kBins - 2)) ++sh;
         const uint32_t base = lo & ~((1u << sh) - 1u);  // (hi - base) >> sh <= kBins - 2
         const Cut c = radix_select<B>(lds, LdsKeys{skey, n}, SampleBinView{lo, hi, base, sh}, want, 0u, kDigitBits, n);
-        return c.value == (uint32_t)(kBins - 1) ? hi + 1u : base + (c.value << sh);
+        return Cutoff{c.value == (uint32_t)(kBins - 1) ? hi + 1u : base + (c.value << sh), shi};
     }
     constexpr int kDropBits = 32 - 2 * kDigitBits;
-    return radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, want, 0u, 2 * kDigitBits, n).value
-           << kDropBits;
+    const uint32_t T =
+        radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, want, 0u, 2 * kDigitBits, n).value
+        << kDropBits;
+    return Cutoff{T, shi};
 }
 
 // ----------------------------------------------------------------------------
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void split_sample_kernel(SplitParams p) {
         kind = kKindAll;
     } else {
         kind = kKindSampled;
-        T = short_cutoff<F32Elem>(p.scores + b * p.row_stride, L, m, skey, SelectLds{hist, found});
+        T = short_cutoff<F32Elem>(p.scores + b * p.row_stride, L, m, skey, SelectLds{hist, found}).T;
     }
     if (threadIdx.x == 0) p.head[b] = SplitHead{0u, 0u, T, kind};
 }
@@ -412,45 +418,68 @@ __global__ __launch_bounds__(kThreads) void split_stream_kernel(SplitParams p) {
     stream_piece(p, b, split_row_len(p, b), h->T, piece, h, p.surv + b * kSplitCapacity, (uint32_t)p.capacity);
 }
 
-// The first pass of a survivor selection: the bin of (key >> shift -
-// base) >> sh, with base aligned to 2^sh, so that bin d holds exactly the
-// keys whose top bits are (base >> sh) + d.
+// The first pass of a survivor selection: keys up to hi in bins of
+// (key >> shift - base) >> sh, base aligned to 2^sh, so that bin d holds
+// exactly the keys up to hi whose top bits are (base >> sh) + d; keys above
+// hi in the top bin.
 template <int kShift>
 struct AboveBinView {
-    uint32_t base;
+    uint32_t base, hi;
     int sh;
     __device__ bool operator()(uint32_t key, uint32_t, uint32_t& v) const {
-        v = ((key >> kShift) - base) >> sh;
+        const uint32_t x = key >> kShift;
+        v = x > hi ? (uint32_t)(kBins - 1) : (x - base) >> sh;
         return true;
     }
 };
+// key >> shift, for the keys in [lo, hi]
+template <int kShift>
+struct ShiftedRangeView {
+    uint32_t lo, hi;
+    __device__ bool operator()(uint32_t key, uint32_t, uint32_t& v) const {
+        v = key >> kShift;
+        return v >= lo && v <= hi;
+    }
+};
 
-// Exact top m of a row's survivors held in LDS by workgroup scope B (keys in
-// [T, vmax]; the short-row and split-finish kernels), ties at the
-// cutoff to the lowest positions, as select_top does, with three savings.
-// Keys are selected on key >> E::kKeyShift, which drops only bits that carry
-// no information (bf16: 16-bit keys). The first pass bins [T, vmax] into at
-// most 2047 bins of equal width (a power of two), so the survivors spread
-// over many bins instead of the few that their top 11 bits share; bins of
-// width 1 settle the cutoff in that pass. And when at most 64 survivors equal
+// Exact top m of a row's survivors held in LDS by workgroup scope B (keys at
+// least T; the short-row and split-finish kernels), ties at the cutoff to the
+// lowest positions, as select_top does, with three savings. Keys are
+// selected on key >> E::kKeyShift, which drops only bits that carry no
+// information (bf16: 16-bit keys). The first pass bins [T, hi] into at most
+// 2047 bins of equal width (a power of two), keys above hi in a top bin of
+// their own, so the survivors spread over many bins instead of the few that
+// their top 11 bits share (bins of width 1 settle the cutoff in that pass);
+// hi need not bound every survivor (the sample's largest finite key serves),
+// and +inf does not stretch the bins. And when at most 64 survivors equal
 // the cutoff key, their positions are gathered and ranked by one wave
 // instead of by radix passes over the positions. `ties` is 66 words of LDS,
 // ties[64] zero on entry.
 template <class E, class B>
 __device__ Selection short_select(SelectLds lds, const PairSource<B>& src, uint32_t m, uint32_t n, uint32_t T,
-                                  uint32_t vmax, int idx_bits, uint32_t* ties) {
+                                  uint32_t hi_key, int idx_bits, uint32_t* ties) {
     constexpr int kShift = E::kKeyShift;
-    const uint32_t lo = T >> kShift, hi = vmax >> kShift;  // every survivor's value lies in [lo, hi]
+    constexpr uint32_t kTop = 0xFFFFFFFFu >> kShift;
+    const uint32_t lo = T >> kShift, hi = max(hi_key >> kShift, lo);
     int sh = 0;
-    while (((hi - lo) >> sh) >= (uint32_t)(kBins - 1)) ++sh;
-    const uint32_t base = sh >= 32 ? 0u : lo & ~((1u << sh) - 1u);  // (hi - base) >> sh < kBins
-    const Cut c1 = radix_select<B>(lds, src, AboveBinView<kShift>{base, sh}, m, 0u, kDigitBits, n);
-    const uint32_t edge = base + (c1.value << sh);  // lowest value in the cutoff bin
-    if (c1.need == c1.equal) return at_least(edge << kShift);  // the bin is taken whole
-    Cut c{edge, c1.need, c1.equal, false};
-    if (sh > 0) {
-        c = radix_select<B>(lds, src, CoarseKeyView<kShift>{}, c1.need, edge, sh, c1.equal);
-        if (c.range) return at_least(c.value << kShift);  // the least full key whose top bits reach c.value
+    while (((hi - lo) >> sh) >= (uint32_t)(kBins - 2)) ++sh;
+    const uint32_t base = lo & ~((1u << sh) - 1u);  // (hi - base) >> sh <= kBins - 2
+    const Cut c1 = radix_select<B>(lds, src, AboveBinView<kShift>{base, hi, sh}, m, 0u, kDigitBits, n);
+    Cut c;
+    if (c1.value == (uint32_t)(kBins - 1)) {  // the cutoff is above hi (so hi < kTop)
+        if (c1.need == c1.equal) return at_least((hi + 1u) << kShift);
+        c = radix_select<B>(lds, src, ShiftedRangeView<kShift>{hi + 1u, kTop}, c1.need, 0u, 32 - kShift, c1.equal);
+        if (c.range) return at_least(c.value << kShift);
+    } else {
+        const uint32_t edge = base + (c1.value << sh);  // lowest value in the cutoff bin
+        if (c1.need == c1.equal) return at_least(edge << kShift);  // the bin is taken whole
+        c = Cut{edge, c1.need, c1.equal, false};
+        if (sh > 0) {
+            // the bin's keys share the bits above sh; keys above hi with
+            // those bits were counted in the top bin, so they stay out
+            c = radix_select<B>(lds, src, ShiftedRangeView<kShift>{edge, hi}, c1.need, edge, sh, c1.equal);
+            if (c.range) return at_least(c.value << kShift);  // the least full key whose top bits reach c.value
+        }
     }
     const uint32_t kth = E::full_key(c.value);
     Selection sel{kth, INT32_MAX};
@@ -568,7 +597,6 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     __shared__ uint32_t count;
     __shared__ uint32_t emitted;
     __shared__ uint32_t ties[66];  // tied positions, their count, the cutoff position
-    __shared__ uint32_t smax;      // the largest survivor key
     static_assert(kShortCap * 2 >= kMaxSample, "the sample fits the survivor buffer");
     const int64_t b = blockIdx.x;
     const int64_t L = split_row_len(p, b);
@@ -584,7 +612,6 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         count = 0u;
         emitted = 0u;
         ties[64] = 0u;
-        smax = 0u;
     }
     B::sync();
     const SelectLds lds{hist, found};
@@ -622,12 +649,12 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         }
     };
     static_assert(kShortCap <= kR * E::kPerVec, "one round covers a row that keeps every score");
-    uint32_t T = 0u;
+    Cutoff cut{0u, 0xFFFFFFFFu};  // a row that keeps every score has no sample
     if (keep_all) load(0, xa);
-    else T = short_cutoff<E>(row, L, m, reinterpret_cast<uint32_t*>(buf), lds, first_loads);
+    else cut = short_cutoff<E>(row, L, m, reinterpret_cast<uint32_t*>(buf), lds, first_loads);
+    const uint32_t T = cut.T;
     B::sync();  // the sample's keys are read; the buffer takes survivors now
 
-    uint32_t hmax = 0u;  // this lane's largest survivor key
     auto filter = [&](const Vec (&x)[kU], int64_t base) {
         uint32_t cnt = 0u;
 #pragma unroll
@@ -644,11 +671,9 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
 #pragma unroll
                 for (int j = 0; j < E::kPerVec; ++j) {
                     const uint32_t bits = E::bits(x[u], j);
-                    const uint32_t key = elem_key<E>(bits);
-                    if (g < nvec && key >= T) {
+                    if (g < nvec && elem_key<E>(bits) >= T) {
                         if (slot < (uint32_t)kShortCap) buf[slot] = make_uint2(bits, (uint32_t)(E::kPerVec * g + j));
                         ++slot;
-                        hmax = max(hmax, key);
                     }
                 }
             }
@@ -670,10 +695,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         const bool hit = i < L && elem_key<E>(bits) >= T;
         const uint32_t slot = wave_reserve_count(&count, hit ? 1u : 0u);
         if (hit && slot < (uint32_t)kShortCap) buf[slot] = make_uint2(bits, (uint32_t)i);
-        if (hit) hmax = max(hmax, elem_key<E>(bits));
     }
-    hmax = wave_max(hmax);
-    if (lane_id() == 0) atomicMax(&smax, hmax);
     B::sync();
     const uint32_t n = count;
     OutRow out = split_out_row(p, b, m, &emitted);
@@ -686,7 +708,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     } else {
         code = keep_all ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
         const PairSource<B> src{buf, n};
-        const Selection s = short_select<E, B>(lds, src, m, n, T, smax, bits_for(L), ties);
+        const Selection s = short_select<E, B>(lds, src, m, n, T, cut.hi, bits_for(L), ties);
         emit(src, s, out);
     }
     if (threadIdx.x == 0) split_stats(p, b, code, n);

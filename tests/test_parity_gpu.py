@@ -533,7 +533,8 @@ def test_short_rows_infinities(topk, n_inf, k):
     # exactly (512), ties at +inf ranked by radix passes (600) or by one wave
     # (50 of k = 40), and more survivors than the buffer holds (5000); as
     # fp32 and as bf16 rows, the last row +inf at its last valid position only
-    # (the block-max kernel's newest block)
+    # (the block-max kernel's newest block); the fp32 rows also through the
+    # split-row entry
     W = 16384
     rng = np.random.default_rng(42 + n_inf)
     x = (rng.standard_normal((4, W)) + 1.4).astype(np.float32)
@@ -545,8 +546,13 @@ def test_short_rows_infinities(topk, n_inf, k):
     synth.poison_tails_bf16(bits, lengths)
     scores = oracle.bf16_to_f32(bits)
     wl = synth.Workload(f"inf{n_inf}", 42, scores, lengths, W, k)
+    want32 = expect(wl)
     got, _ = run(topk, wl)
-    assert_parity(wl, got, expect(wl))
+    assert_parity(wl, got, want32)
+    say(f"  gpu split call: inf{n_inf} k={k}")
+    out_s = topk.topk_select_split(to_dev(wl.scores), to_dev(wl.lengths), k)
+    torch.cuda.synchronize()
+    assert_parity(wl, out_s.cpu().numpy(), want32)
     s = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
     say(f"  gpu bf16 call: inf{n_inf} k={k}")
     out = topk.topk_select_bf16(s, torch.from_numpy(lengths).cuda(), k)

@@ -109,6 +109,12 @@ def _device_ptr(t: torch.Tensor | None, name: str, dtype: torch.dtype):
     return t.data_ptr()
 
 
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and isinstance(t, torch.Tensor) and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, scores on {device}")
+
+
 def _stream_handle(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -136,7 +142,11 @@ def _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream, dty
         if page_table.dim() != 2 or page_table.size(0) != batch or (
                 page_table.size(1) > 1 and page_table.stride(1) != 1):
             raise ValueError("page_table must be [batch, pages] with unit column stride")
+        if page_size >= 1 and page_table.size(1) < -(-n_cols // page_size):
+            raise ValueError(f"page_table has {page_table.size(1)} columns; rows of {n_cols} scores "
+                             f"span {-(-n_cols // page_size)} pages of {page_size}")
         pt_stride = page_table.stride(0) if batch > 1 else page_table.size(1)
+    _same_device(scores.device, lengths=lengths, out=out, page_table=page_table)
     handle = _stream_handle(stream, scores.device)
     args = (
         _device_ptr(scores, "scores", dtype), batch, row_stride, n_cols,
@@ -180,6 +190,7 @@ def topk_select_ex(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
     args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream)
     if row_stats is not None and (row_stats.shape != (scores.size(0), 2) or not row_stats.is_contiguous()):
         raise ValueError("row_stats must be a contiguous [batch, 2] tensor")
+    _same_device(scores.device, row_stats=row_stats)
     opt = _Options(int(force_path), int(capacity), _device_ptr(row_stats, "row_stats", torch.int32))
     _check(_load().topk_select_ex(*args, ctypes.byref(opt)))
     return out
@@ -214,6 +225,7 @@ def topk_select_split(scores: torch.Tensor, lengths: torch.Tensor | None, k: int
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=scores.device)
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
+    _same_device(scores.device, workspace=workspace, row_stats=row_stats)
     opt = _Options(int(force_path), int(capacity), _device_ptr(row_stats, "row_stats", torch.int32))
     status = _load().topk_select_split(*args[:-1], _device_ptr(workspace, "workspace", torch.uint8),
                                        workspace.numel(), int(pieces), args[-1], ctypes.byref(opt))
@@ -237,13 +249,16 @@ def topk_select_bf16(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
 
 def amax8_varlen(scores: torch.Tensor, lengths: torch.Tensor | None, topk: int = 0, *,
                  max_seqlen: int = 0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Level-one keys of the two-level indexer: ``out[b, i]`` is the largest of
-    ``scores[b, 8i : 8i + 8]`` (NaN ignored, +0 above -0) for
-    ``i < ceil(lengths[b] / 8) - 1``, ``+inf`` at the newest block, nothing
-    past it; rows with at most ``topk`` blocks are left alone (``topk=0``
-    never skips). ``out`` is ``[batch, ceil(max_seqlen / 8)]`` fp32, allocated
-    (uninitialised) when omitted; ``max_seqlen`` defaults to the width of
-    ``scores``, and lengths are clamped to it."""
+    """Block keys for the indexer's first stage (the block-max kernel of
+    "dsv4.1: Top-k kernels and candidate selection", implementation section 2;
+    signature kept from that page's entry so callers can switch). Row b's
+    first L = clamp(lengths[b], 0, max_seqlen) scores form ceil(L / 8) blocks
+    of 8; each block but the last gets its largest score (NaN skipped, +0
+    ranked above -0), the last gets +inf, and later columns are not written.
+    With ``topk > 0`` a row of at most ``topk`` blocks is not written at all;
+    ``topk = 0`` writes every row. ``out`` is fp32 ``[batch, >= ceil(max_seqlen
+    / 8)]``, allocated uninitialised when omitted; ``max_seqlen`` = 0 means
+    the width of ``scores``."""
     if scores.dim() != 2 or (scores.size(1) > 1 and scores.stride(1) != 1):
         raise ValueError("scores must be 2-D with unit column stride")
     batch = scores.size(0)
@@ -256,6 +271,7 @@ def amax8_varlen(scores: torch.Tensor, lengths: torch.Tensor | None, topk: int =
         raise ValueError("out must be [batch, blocks] with unit column stride")
     if lengths is not None and (lengths.dim() != 1 or lengths.size(0) != batch or not lengths.is_contiguous()):
         raise ValueError("lengths must be a contiguous [batch] tensor")
+    _same_device(scores.device, lengths=lengths, out=out)
     row_stride = scores.stride(0) if batch > 1 else max(scores.size(1), 1)
     out_stride = out.stride(0) if batch > 1 else out.size(1)
     _check(_load().amax8_varlen(_device_ptr(scores, "scores", torch.float32), batch, row_stride, n_cols,
@@ -289,6 +305,10 @@ def sort_candidate_blocks(blocks: torch.Tensor, lengths: torch.Tensor | None, pa
     bpp = max(page_size // 8, 1)
     if n_cols is None:
         n_cols = 8 * page_table.size(1) * bpp
+    if page_table.size(1) < -(-(-(-n_cols // 8)) // bpp):
+        raise ValueError(f"page_table has {page_table.size(1)} columns; rows of {n_cols} positions "
+                         f"span {-(-(-(-n_cols // 8)) // bpp)} pages of {bpp} blocks")
+    _same_device(blocks.device, lengths=lengths, page_table=page_table, out_pages=out_pages)
     pt_stride = page_table.stride(0) if batch > 1 else page_table.size(1)
     _check(_load().sort_candidate_blocks(_device_ptr(blocks, "blocks", torch.int32), batch, int(k),
                                          _device_ptr(lengths, "lengths", torch.int32), int(n_cols),

@@ -172,23 +172,25 @@ def _block_max(blocks: np.ndarray) -> np.ndarray:
 
 
 def amax8(scores: np.ndarray, lengths, topk: int, out: np.ndarray, *, n_cols: int | None = None) -> np.ndarray:
-    """Level-one keys of the two-level indexer ("dsv4.1: Top-k kernels and
-    candidate selection", implementation section 2, block-max kernel, and
-    code excerpts, docstring of amax8_varlen), written into ``out`` in place.
+    """Block keys for the first stage of the two-level indexer, as defined for
+    the block-max kernel on "dsv4.1: Top-k kernels and candidate selection"
+    (implementation section 2 and the ``amax8_varlen`` entry among the code
+    excerpts). Written into ``out`` in place.
 
-    Per row b, with L = clamp(lengths[b], 0, n_cols) (n_cols defaults to the
-    width of ``scores``) and nb = ceil(L / 8) blocks:
-    ``out[b, i]`` = the largest of ``scores[b, 8i : 8i + 8]`` for i < nb - 1
-    (NaN ignored, +0 above -0; NaN only for an all-NaN block),
-    ``out[b, nb - 1] = +inf`` (the newest block is always selected), and
-    nothing is written past nb. With ``topk > 0``, a row with nb <= topk is
-    left untouched (all its blocks are selected anyway). ``out`` needs at
-    least ceil(n_cols / 8) columns.
+    Row b keeps L = clamp(lengths[b], 0, n_cols) scores (``lengths`` None:
+    every row n_cols; n_cols defaults to the width of ``scores``), grouped
+    into nb = ceil(L / 8) blocks of 8. Block i < nb - 1 gets the largest of
+    its 8 scores, ranking +0 above -0 and skipping NaN (an all-NaN block
+    gives NaN). Block nb - 1, the most recent one, is set to +inf so that a
+    later top-k always keeps it. Columns from nb on are not touched, and
+    neither is any row whose nb is at most ``topk`` when ``topk > 0``,
+    since such a row keeps every block. ``out`` needs at least
+    ceil(n_cols / 8) columns.
     """
     scores = np.asarray(scores, dtype=np.float32)
     n_cols = scores.shape[1] if n_cols is None else n_cols
     for b in range(scores.shape[0]):
-        L = min(max(int(lengths[b]), 0), n_cols)
+        L = n_cols if lengths is None else min(max(int(lengths[b]), 0), n_cols)
         nb = -(-L // 8)
         if nb > out.shape[1] or L > scores.shape[1]:
             raise ValueError("a row's blocks do not fit the output or its scores")
@@ -204,28 +206,34 @@ INT32_MAX = 2**31 - 1
 
 
 def sort_candidate_blocks(blocks: np.ndarray, lengths, page_table: np.ndarray,
-                          page_size: int):
-    """The block table of the two-level indexer ("dsv4.1: Top-k kernels and
-    candidate selection", implementation section 2, candidate-block-table
-    kernel, and code excerpts, docstring of sort_candidate_blocks).
+                          page_size: int, *, n_cols: int):
+    """Candidate block table of the two-level indexer, as defined for the
+    block-table kernel on "dsv4.1: Top-k kernels and candidate selection"
+    (implementation section 2 and the ``sort_candidate_blocks`` entry among
+    the code excerpts).
 
-    Per row b, with nb = ceil(max(lengths[b], 0) / 8) and k = blocks.shape[1]:
-    if nb <= k the table is the identity 0 .. nb-1 whatever the input;
-    otherwise it is the distinct ids among the row's k entries that lie in
-    [0, nb), ascending (for a top-k selection that is all k of them). Slots
-    past the table hold INT32_MAX. ``pages[b, j]`` is the pool slot of the
-    j-th id: ``page_table[b, id // bpp] * bpp + id % bpp`` with
-    ``bpp = page_size // 8``, INT32_MAX where the table is padded.
+    Row b holds k = blocks.shape[1] block ids. Its length is clamped like
+    every other length on the path, L = clamp(lengths[b], 0, n_cols)
+    (``lengths`` None: every row n_cols), and it spans nb = ceil(L / 8)
+    blocks. With nb <= k the result is 0 .. nb-1 and the ids given are
+    ignored; with nb > k it is the distinct given ids inside [0, nb), in
+    increasing order (all k of them when the ids come from a top-k
+    selection). INT32_MAX pads the rest of the row. The page output maps id
+    to ``page_table[b, id // bpp] * bpp + id % bpp`` with
+    ``bpp = page_size // 8`` and carries the same padding.
     Returns ``(table, pages)``, both int32 ``[batch, k]``.
     """
     if page_size < 8 or page_size & (page_size - 1):
         raise ValueError("page_size must be a power of two, at least 8")
+    if n_cols < 0:
+        raise ValueError("n_cols must be non-negative")
     bpp = page_size // 8
     B, k = blocks.shape
     table = np.full((B, k), INT32_MAX, dtype=np.int32)
     pages = np.full((B, k), INT32_MAX, dtype=np.int32)
     for b in range(B):
-        nb = -(-max(int(lengths[b]), 0) // 8)
+        L = n_cols if lengths is None else min(max(int(lengths[b]), 0), n_cols)
+        nb = -(-L // 8)
         if nb <= k:
             ids = np.arange(nb, dtype=np.int64)
         else:

@@ -189,3 +189,20 @@ def test_indexer_host_argument_checks(lib):
     assert sb(ps=48) == 1 and sb(ps=4) == 1 and sb(pts=127) == 1 and sb(k=0) == 1
     assert sb(n=2**21 + 1, pts=2**20) == 1 and sb(pt=None) == 1 and sb(out=None) == 1
     assert sb(batch=0, blocks=None, pt=None, out=None) == 0
+
+
+def test_binding_rejects_narrow_page_tables():
+    # the binding checks page-table widths before taking any pointer, so CPU
+    # tensors reach the check; a column slice keeps its row stride, so the C
+    # side's stride check alone would accept it
+    import torch
+
+    import exact_row_top_fp32_amd as topk
+
+    scores = torch.zeros((4, 1000))
+    pt = torch.zeros((4, 40), dtype=torch.int32)[:, :15]  # 1000 scores span 16 pages of 64
+    with pytest.raises(ValueError, match="page_table"):
+        topk.topk_select(scores, None, 8, page_table=pt, page_size=64)
+    blocks = torch.zeros((4, 8), dtype=torch.int32)
+    with pytest.raises(ValueError, match="page_table"):  # 1000 positions: 125 blocks, 16 pages of 8
+        topk.sort_candidate_blocks(blocks, None, pt, 64, n_cols=1000)

@@ -152,7 +152,7 @@ def test_graph_replay_of_the_indexer_chain_and_bf16_topk(topk):
         oracle.amax8(x, lens, k, want_keys)
         assert np.array_equal(keys.cpu().numpy().view(np.uint32), want_keys.view(np.uint32))
         nb_h = ((np.maximum(lens, 0).astype(np.int64) + 7) // 8).astype(np.int32)
-        table, slots = oracle.sort_candidate_blocks(oracle.topk(want_keys, nb_h, k), lens, pt_h, ps)
+        table, slots = oracle.sort_candidate_blocks(oracle.topk(want_keys, nb_h, k), lens, pt_h, ps, n_cols=W)
         assert np.array_equal(blocks.cpu().numpy(), table)
         assert np.array_equal(pages.cpu().numpy(), slots)
         want_b = oracle.topk_bf16(bits, lens_b, kb)

@@ -165,6 +165,31 @@ def test_amax8_all_nan_and_signed_zero_blocks(topk):
     assert np.isnan(got[0, 1]) and got[0, 2] == 0 and not np.signbit(got[0, 2]) and np.signbit(got[0, 3])
 
 
+def test_amax8_lengths_past_n_cols(topk):
+    # n_cols below the width of the storage, lengths past it: each row acts as
+    # if its length were n_cols; the scores past n_cols are large, so reading
+    # any of them would show in the keys
+    W, stride = 4096 + 19 * 8 + 3, 4096 + 64 * 8
+    lens = np.array([W, W + 1, W + 7, W + 8, W + 300, 2**31 - 1, W - 1, 0], np.int32)
+    rng = np.random.default_rng(70)
+    x = rng.standard_normal((lens.size, stride)).astype(np.float32)
+    x[:, W:] = 1e30
+    for topk_k in (0, 300, W // 8):
+        s = torch.from_numpy(x).cuda()
+        ln = torch.from_numpy(lens).cuda()
+        cols = stride // 8
+        buf, out = guarded((lens.size, cols), torch.float32, -7.0)
+        say(f"  gpu amax8 call: lengths past n_cols={W}, topk={topk_k}")
+        topk.amax8_varlen(s, ln, topk_k, max_seqlen=W, out=out)
+        torch.cuda.synchronize()
+        assert guards_intact(buf, -7.0), "write outside out"
+        want = np.full((lens.size, cols), -7.0, np.float32)
+        oracle.amax8(x, lens, topk_k, want, n_cols=W)
+        got = out.cpu().numpy()
+        bad = np.flatnonzero(np.any(got.view(np.uint32) != want.view(np.uint32), axis=1))
+        assert bad.size == 0, f"rows differing bit for bit: {bad[:10]}"
+
+
 # ----------------------------------------------------------------------------
 # candidate block table
 # ----------------------------------------------------------------------------
@@ -178,7 +203,7 @@ def run_table(topk, wl, n_cols):
     topk.sort_candidate_blocks(blocks, ln, pt, wl.page_size, out_pages=pages, n_cols=n_cols)
     torch.cuda.synchronize()
     assert guards_intact(buf, CANARY), "write outside out_pages"
-    table, slots = oracle.sort_candidate_blocks(wl.blocks, wl.lengths, wl.page_table, wl.page_size)
+    table, slots = oracle.sort_candidate_blocks(wl.blocks, wl.lengths, wl.page_table, wl.page_size, n_cols=n_cols)
     got_t, got_p = blocks.cpu().numpy(), pages.cpu().numpy()
     bad = np.flatnonzero(np.any(got_t != table, axis=1) | np.any(got_p != slots, axis=1))
     assert bad.size == 0, f"rows differing: {bad[:10]}"
@@ -205,6 +230,21 @@ def test_block_table_junk_entries_and_large_rows(topk):
     pt = np.stack([rng.permutation(W // 64) for _ in lens]).astype(np.int32)
     wl = synth.BlockTableWorkload("blocks_junk", 68, blocks, lens, pt, 64)
     run_table(topk, wl, W)
+
+
+def test_block_table_lengths_past_n_cols(topk):
+    # lengths past n_cols count as n_cols: ids at or past ceil(n_cols / 8) are
+    # dropped, and a row whose clamped block count is at most k takes the
+    # identity table whatever its length says
+    rng = np.random.default_rng(71)
+    k, ps = 64, 64
+    for n_cols in (8 * 500 + 3, 8 * 64, 8 * 64 + 1):
+        nb = -(-n_cols // 8)
+        lens = np.array([n_cols, n_cols + 1, n_cols + 8, n_cols + 5000, 2**31 - 1, n_cols - 9, -2], np.int32)
+        blocks = np.stack([rng.choice(nb + 200, k, replace=False) for _ in lens]).astype(np.int32)
+        pt = np.stack([rng.permutation(-(-(nb + 200) // (ps // 8))) for _ in lens]).astype(np.int32)
+        wl = synth.BlockTableWorkload(f"blocks_past_n_cols_{n_cols}", 71, blocks, lens, pt, ps)
+        run_table(topk, wl, n_cols)
 
 
 # ----------------------------------------------------------------------------
@@ -242,6 +282,6 @@ def test_two_level_indexer_chain(topk, c3):
     assert np.array_equal(keys.cpu().numpy().view(np.uint32), want_keys.view(np.uint32))
     nb_h = nb.cpu().numpy()
     want_sel = oracle.topk(want_keys, nb_h, k)
-    table, slots = oracle.sort_candidate_blocks(want_sel, lengths, pt_h, ps)
+    table, slots = oracle.sort_candidate_blocks(want_sel, lengths, pt_h, ps, n_cols=c3.n_cols)
     assert np.array_equal(blocks.cpu().numpy(), table)
     assert np.array_equal(pages.cpu().numpy(), slots)

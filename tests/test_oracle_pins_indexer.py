@@ -141,12 +141,13 @@ def pin_amax_brute_force(fn, seed=71, cases=300):
     rng = np.random.default_rng(seed)
     for _ in range(cases):
         W = 8 * int(rng.integers(1, 7))
-        L = int(rng.integers(-2, W + 1))
+        n_cols = int(rng.integers(0, W + 1))  # the scores past n_cols are never read
+        L = int(rng.integers(-2, W + 12))
         topk = int(rng.integers(0, 4))
         x = rng.choice(AMAX_ALPHABET, (1, W)).astype(np.float32)
-        out = np.full((1, W // 8 + 1), 77.0, np.float32)
-        fn(x, np.array([L], np.int32), topk, out)
-        nb = -(-max(L, 0) // 8)
+        out = np.full((1, W // 8 + 3), 77.0, np.float32)
+        fn(x, np.array([L], np.int32), topk, out, n_cols=n_cols)
+        nb = -(-min(max(L, 0), n_cols) // 8)
         skipped = nb == 0 or (topk > 0 and nb <= topk)
         for i in range(out.shape[1]):
             if skipped or i >= nb:
@@ -184,7 +185,30 @@ def pin_amax_closed_forms(fn):
     assert np.all(out[0] == -5) and out[1, 3] == np.inf and out[1, 0] == 7
 
 
-AMAX_PINS = [pin_amax_brute_force, pin_amax_torch, pin_amax_closed_forms]
+def pin_amax_length_clamp(fn):
+    """Lengths past n_cols act as n_cols: on ascending rows block i holds
+    8 i + 7, the block at ceil(n_cols / 8) - 1 is +inf and nothing later is
+    written, even though the row's storage goes on with larger values."""
+    W = 128
+    for n_cols in (80, 83, 121):
+        nb = -(-n_cols // 8)
+        lens = np.array([n_cols, n_cols + 1, n_cols + 7, n_cols + 8, n_cols + 40, 2**31 - 1], np.int32)
+        x = np.arange(W, dtype=np.float32)[None, :].repeat(lens.size, 0)
+        x[:, n_cols:] = 1e30
+        out = np.full((lens.size, W // 8 + 2), -5.0, np.float32)
+        fn(x, lens, 0, out, n_cols=n_cols)
+        want = np.full(W // 8 + 2, -5.0, np.float32)
+        want[:nb - 1] = 8 * np.arange(nb - 1) + 7
+        want[nb - 1] = np.inf
+        for b in range(lens.size):
+            assert np.array_equal(out[b], want), (n_cols, int(lens[b]), out[b])
+        # the skip rule counts the clamped blocks
+        out = np.full((1, W // 8 + 2), -5.0, np.float32)
+        fn(x[:1], np.array([n_cols + 60], np.int32), nb, out, n_cols=n_cols)
+        assert np.all(out == -5.0)
+
+
+AMAX_PINS = [pin_amax_brute_force, pin_amax_torch, pin_amax_closed_forms, pin_amax_length_clamp]
 
 
 # ----------------------------------------------------------------------------
@@ -210,7 +234,7 @@ def pin_blocks_invariants(fn, seed=81, cases=200):
             row = rng.integers(-1, nb + 3, k).astype(np.int32)
         pages = -(-max(nb, 1) // bpp) + 1
         pt = (rng.permutation(pages) + 1000).astype(np.int32)[None, :]
-        table, slots = fn(row[None, :].copy(), np.array([L], np.int32), pt, ps)
+        table, slots = fn(row[None, :].copy(), np.array([L], np.int32), pt, ps, n_cols=8 * 3 * k)
         want = list(range(nb)) if nb <= k else sorted(set(v for v in row.tolist() if 0 <= v < nb))
         n = len(want)
         assert table[0, :n].tolist() == want and np.all(table[0, n:] == INT32_MAX)
@@ -226,7 +250,7 @@ def pin_blocks_identity_pages(fn):
     k, L = 64, 8 * 1000
     row = rng.choice(1000, k, replace=False).astype(np.int32)[None, :]
     pt = np.arange(200, dtype=np.int32)[None, :]
-    table, slots = fn(row, np.array([L], np.int32), pt, 64)
+    table, slots = fn(row, np.array([L], np.int32), pt, 64, n_cols=L)
     assert np.array_equal(table[0], np.sort(row[0])) and np.array_equal(slots[0], table[0])
 
 
@@ -236,14 +260,33 @@ def pin_blocks_short_rows(fn):
     rows = np.full((3, k), 999, np.int32)
     rows[1] = -1
     pt = np.tile(np.arange(20, dtype=np.int32)[::-1], (3, 1))
-    table, slots = fn(rows, np.array([8 * k, 8 * 5 - 7, 0], np.int32), pt, 8)
+    table, slots = fn(rows, np.array([8 * k, 8 * 5 - 7, 0], np.int32), pt, 8, n_cols=8 * 20)
     assert table[0].tolist() == list(range(k))
     assert table[1, :5].tolist() == list(range(5)) and np.all(table[1, 5:] == INT32_MAX)
     assert np.all(table[2] == INT32_MAX) and np.all(slots[2] == INT32_MAX)
     assert slots[0].tolist() == [19 - i for i in range(k)]
 
 
-BLOCK_PINS = [pin_blocks_invariants, pin_blocks_identity_pages, pin_blocks_short_rows]
+def pin_blocks_length_clamp(fn):
+    """Lengths past n_cols act as n_cols. With n_cols = 323 a row spans 41
+    blocks: ids 41 and up are dropped from a selection however long the row
+    claims to be. With n_cols = 128 and k = 16 a row spans 16 <= k blocks, so
+    its table is the identity whatever it holds and whatever its length."""
+    k = 16
+    given = np.array([40, 3, 41, 0, 17, 42, 99, 5, 39, 200, 1, 6, 2, 60, 7, 8], np.int32)
+    want = sorted(v for v in given.tolist() if v < 41)
+    lens = np.array([323, 324, 330, 1000, 2**31 - 1], np.int32)
+    pt = np.tile(np.arange(100, dtype=np.int32) + 500, (lens.size, 1))
+    table, slots = fn(np.tile(given, (lens.size, 1)), lens, pt, 8, n_cols=323)
+    for b in range(lens.size):
+        assert table[b, :len(want)].tolist() == want and np.all(table[b, len(want):] == INT32_MAX)
+        assert slots[b, :len(want)].tolist() == [500 + v for v in want]
+    table, slots = fn(np.tile(given, (3, 1)), np.array([128, 129, 5000], np.int32), pt[:3], 8, n_cols=128)
+    assert np.array_equal(table, np.tile(np.arange(k, dtype=np.int32), (3, 1)))
+    assert np.array_equal(slots, table + 500)
+
+
+BLOCK_PINS = [pin_blocks_invariants, pin_blocks_identity_pages, pin_blocks_short_rows, pin_blocks_length_clamp]
 
 
 # ----------------------------------------------------------------------------
@@ -295,9 +338,14 @@ def bf16_mutant(mutation):
 
 
 def amax_mutant(mutation):
-    def fn(scores, lengths, topk, out):
+    def fn(scores, lengths, topk, out, n_cols=None):
+        n_cols = scores.shape[1] if n_cols is None else n_cols
         for b in range(scores.shape[0]):
             L = max(int(lengths[b]), 0)
+            if mutation == "clamp_to_width":
+                L = min(L, scores.shape[1])
+            elif mutation != "no_upper_clamp":
+                L = min(L, n_cols)
             nb = L // 8 if mutation == "floor_blocks" else -(-L // 8)
             if nb == 0 or (topk > 0 and (nb < topk if mutation == "skip_strict" else nb <= topk)):
                 continue
@@ -319,13 +367,15 @@ def amax_mutant(mutation):
 
 
 def blocks_mutant(mutation):
-    def fn(blocks, lengths, page_table, page_size):
+    def fn(blocks, lengths, page_table, page_size, n_cols):
         bpp = page_size if mutation == "bpp_is_page_size" else page_size // 8
         B, k = blocks.shape
         table = np.full((B, k), INT32_MAX, np.int32)
         pages = np.full((B, k), INT32_MAX, np.int32)
         for b in range(B):
-            nb = -(-max(int(lengths[b]), 0) // 8)
+            L = max(int(lengths[b]), 0)
+            L = L if mutation == "no_upper_clamp" else min(L, n_cols + 8 if mutation == "clamp_one_block_late" else n_cols)
+            nb = -(-L // 8)
             ident = nb < k if mutation == "identity_strict" else nb <= k
             if ident:
                 ids = list(range(nb))
@@ -362,11 +412,12 @@ def test_bf16_pins_reject_planted_mistakes(mutation):
 
 
 @pytest.mark.parametrize("mutation", ["floor_blocks", "skip_strict", "nan_propagates", "minus_zero_wins",
-                                      "no_inf_newest"])
+                                      "no_inf_newest", "no_upper_clamp", "clamp_to_width"])
 def test_amax8_pins_reject_planted_mistakes(mutation):
     assert caught_by(AMAX_PINS, amax_mutant(mutation))
 
 
-@pytest.mark.parametrize("mutation", ["bpp_is_page_size", "identity_strict", "keep_minus_one", "descending"])
+@pytest.mark.parametrize("mutation", ["bpp_is_page_size", "identity_strict", "keep_minus_one", "descending",
+                                      "no_upper_clamp", "clamp_one_block_late"])
 def test_block_table_pins_reject_planted_mistakes(mutation):
     assert caught_by(BLOCK_PINS, blocks_mutant(mutation))

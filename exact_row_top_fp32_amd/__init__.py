@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "topk_select", "topk_select_ex", "topk_select_split", "topk_split_workspace_bytes",
     "topk_split_capacity", "topk_select_bf16", "amax8_varlen", "sort_candidate_blocks",
-    "topk_status_string", "topk_max_capacity", "topk_watchdog_trips",
+    "topk_select_bf16_ex", "topk_status_string", "topk_max_capacity", "topk_short_capacity",
+    "topk_watchdog_trips", "KERNEL_AUTO", "KERNEL_PERSISTENT", "KERNEL_SHORT",
     "TopKError", "library_path", "PATH_AUTO", "PATH_LDS", "PATH_SAMPLED", "PATH_FULLROW",
     "ROW_EMPTY", "ROW_ALL", "ROW_LDS", "ROW_SAMPLED", "ROW_FULL_OVERFLOW",
     "ROW_FULL_UNDERFLOW", "ROW_FULL_FORCED", "MAX_K",
@@ -27,6 +28,7 @@ library_path = os.path.join(_PKG, "libexact_topk.so")
 
 MAX_K = 2048
 PATH_AUTO, PATH_LDS, PATH_SAMPLED, PATH_FULLROW = 0, 1, 2, 3
+KERNEL_AUTO, KERNEL_PERSISTENT, KERNEL_SHORT = 0, 1, 2
 (ROW_EMPTY, ROW_ALL, ROW_LDS, ROW_SAMPLED, ROW_FULL_OVERFLOW, ROW_FULL_UNDERFLOW,
  ROW_FULL_FORCED) = range(7)
 
@@ -39,7 +41,7 @@ class TopKError(RuntimeError):
 
 class _Options(ctypes.Structure):
     _fields_ = [("force_path", ctypes.c_int32), ("capacity", ctypes.c_int32),
-                ("row_stats", ctypes.c_void_p)]
+                ("row_stats", ctypes.c_void_p), ("kernel", ctypes.c_int32)]
 
 
 _lib = None
@@ -63,6 +65,8 @@ def _load():
         lib.topk_status_string.argtypes = [ctypes.c_int]
         lib.topk_max_capacity.restype = ctypes.c_int32
         lib.topk_max_capacity.argtypes = []
+        lib.topk_short_capacity.restype = ctypes.c_int32
+        lib.topk_short_capacity.argtypes = []
         lib.topk_watchdog_trips.restype = ctypes.c_uint32
         lib.topk_watchdog_trips.argtypes = []
         lib.topk_select_split.restype = ctypes.c_int
@@ -74,6 +78,8 @@ def _load():
         lib.topk_split_capacity.argtypes = []
         lib.topk_select_bf16.restype = ctypes.c_int
         lib.topk_select_bf16.argtypes = _ARGS
+        lib.topk_select_bf16_ex.restype = ctypes.c_int
+        lib.topk_select_bf16_ex.argtypes = _ARGS + [ctypes.POINTER(_Options)]
         lib.amax8_varlen.restype = ctypes.c_int
         lib.amax8_varlen.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
@@ -92,6 +98,10 @@ def topk_status_string(status: int) -> str:
 
 def topk_max_capacity() -> int:
     return int(_load().topk_max_capacity())
+
+
+def topk_short_capacity() -> int:
+    return int(_load().topk_short_capacity())
 
 
 def topk_watchdog_trips() -> int:
@@ -177,21 +187,26 @@ def topk_select(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
     return out
 
 
+def _options(scores, force_path, capacity, row_stats, kernel):
+    if row_stats is not None and (row_stats.shape != (scores.size(0), 2) or not row_stats.is_contiguous()):
+        raise ValueError("row_stats must be a contiguous [batch, 2] tensor")
+    _same_device(scores.device, row_stats=row_stats)
+    return _Options(int(force_path), int(capacity), _device_ptr(row_stats, "row_stats", torch.int32), int(kernel))
+
+
 def topk_select_ex(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
                    out: torch.Tensor | None = None, page_table: torch.Tensor | None = None,
                    page_size: int = 0, *, n_cols: int | None = None, stream=None,
                    force_path: int = PATH_AUTO, capacity: int = 0,
-                   row_stats: torch.Tensor | None = None) -> torch.Tensor:
-    """``topk_select`` with path forcing, a capacity override and row statistics.
+                   row_stats: torch.Tensor | None = None, kernel: int = KERNEL_AUTO) -> torch.Tensor:
+    """``topk_select`` with path forcing, a capacity override, row statistics
+    and a kernel choice.
 
     ``row_stats`` (int32 ``[batch, 2]``, contiguous) receives the path code
     and the sampled survivor count (or the length) of every row.
     """
     args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream)
-    if row_stats is not None and (row_stats.shape != (scores.size(0), 2) or not row_stats.is_contiguous()):
-        raise ValueError("row_stats must be a contiguous [batch, 2] tensor")
-    _same_device(scores.device, row_stats=row_stats)
-    opt = _Options(int(force_path), int(capacity), _device_ptr(row_stats, "row_stats", torch.int32))
+    opt = _options(scores, force_path, capacity, row_stats, kernel)
     _check(_load().topk_select_ex(*args, ctypes.byref(opt)))
     return out
 
@@ -218,15 +233,13 @@ def topk_select_split(scores: torch.Tensor, lengths: torch.Tensor | None, k: int
     omitted); ``pieces`` is the number of workgroups per row (0 = automatic).
     """
     args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream)
-    if row_stats is not None and (row_stats.shape != (scores.size(0), 2) or not row_stats.is_contiguous()):
-        raise ValueError("row_stats must be a contiguous [batch, 2] tensor")
+    opt = _options(scores, force_path, capacity, row_stats, KERNEL_AUTO)
     need = topk_split_workspace_bytes(scores.size(0))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=scores.device)
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
-    _same_device(scores.device, workspace=workspace, row_stats=row_stats)
-    opt = _Options(int(force_path), int(capacity), _device_ptr(row_stats, "row_stats", torch.int32))
+    _same_device(scores.device, workspace=workspace)
     status = _load().topk_select_split(*args[:-1], _device_ptr(workspace, "workspace", torch.uint8),
                                        workspace.numel(), int(pieces), args[-1], ctypes.byref(opt))
     _check(status)
@@ -244,6 +257,22 @@ def topk_select_bf16(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
     args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream,
                          dtype=torch.bfloat16)
     _check(_load().topk_select_bf16(*args))
+    return out
+
+
+def topk_select_bf16_ex(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
+                        out: torch.Tensor | None = None, page_table: torch.Tensor | None = None,
+                        page_size: int = 0, *, n_cols: int | None = None, stream=None,
+                        force_path: int = PATH_AUTO, capacity: int = 0,
+                        row_stats: torch.Tensor | None = None) -> torch.Tensor:
+    """``topk_select_bf16`` with path forcing, a capacity override (at most
+    ``topk_short_capacity()``) and row statistics, as ``topk_select_ex``."""
+    if scores.dtype != torch.bfloat16:
+        raise TypeError(f"scores must be torch.bfloat16, got {scores.dtype}")
+    args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream,
+                         dtype=torch.bfloat16)
+    opt = _options(scores, force_path, capacity, row_stats, KERNEL_AUTO)
+    _check(_load().topk_select_bf16_ex(*args, ctypes.byref(opt)))
     return out
 
 

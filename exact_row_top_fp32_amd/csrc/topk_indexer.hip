@@ -176,13 +176,18 @@ using namespace topk;
 
 extern "C" {
 
-int topk_select_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
-                     const int32_t* lengths, int32_t k, int32_t* out_idx,
-                     const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
-                     void* hip_stream) {
+int topk_select_bf16_ex(const uint16_t* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                        const int32_t* lengths, int32_t k, int32_t* out_idx,
+                        const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                        void* hip_stream, const topk_options* options) {
     if (batch < 0 || batch > (int64_t)(UINT32_MAX / 256)) return TOPK_ERR_ARG;
     if (k < 1 || k > TOPK_MAX_K) return TOPK_ERR_K;
     if (n_cols < 0 || n_cols > kBfMaxCols || row_stride < n_cols) return TOPK_ERR_ARG;
+    topk_options opt{TOPK_PATH_AUTO, 0, nullptr, TOPK_KERNEL_AUTO};
+    if (options != nullptr) opt = *options;
+    if (opt.force_path < TOPK_PATH_AUTO || opt.force_path > TOPK_PATH_FULLROW) return TOPK_ERR_ARG;
+    if (opt.capacity < 0 || opt.capacity > kShortCapacity) return TOPK_ERR_ARG;
+    if (opt.kernel != TOPK_KERNEL_AUTO && opt.kernel != TOPK_KERNEL_SHORT) return TOPK_ERR_ARG;
     if (page_table != nullptr) {
         if (page_size < 1) return TOPK_ERR_ARG;
         if (page_table_stride < (n_cols + page_size - 1) / page_size) return TOPK_ERR_ARG;
@@ -191,8 +196,17 @@ int topk_select_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, 
     if (scores == nullptr || out_idx == nullptr) return TOPK_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(scores) & 15u) != 0) return TOPK_ERR_ALIGN;
     if (batch > 1 && (row_stride & 7) != 0) return TOPK_ERR_ALIGN;
+    if (device_cus() <= 0) return TOPK_ERR_DEVICE;
     return launch_short_rows_bf16(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
-                                  page_table_stride, page_size, static_cast<hipStream_t>(hip_stream));
+                                  page_table_stride, page_size, opt, static_cast<hipStream_t>(hip_stream));
+}
+
+int topk_select_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                     const int32_t* lengths, int32_t k, int32_t* out_idx,
+                     const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                     void* hip_stream) {
+    return topk_select_bf16_ex(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
+                               page_table_stride, page_size, hip_stream, nullptr);
 }
 
 int amax8_varlen(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols, const int32_t* lengths,
@@ -207,6 +221,7 @@ int amax8_varlen(const float* scores, int64_t batch, int64_t row_stride, int64_t
     if (batch > 1 && (row_stride & 7) != 0) return TOPK_ERR_ALIGN;
     const int64_t tiles = (blocks + kAmaxTile - 1) / kAmaxTile;
     if (batch * tiles * kAmaxThreads > (int64_t)UINT32_MAX) return TOPK_ERR_ARG;
+    if (device_cus() <= 0) return TOPK_ERR_DEVICE;
     Amax8Params p{scores, row_stride, n_cols, lengths, topk, out, out_stride, tiles};
     void* args[] = {&p};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&amax8_kernel), dim3((uint32_t)(batch * tiles)),
@@ -225,6 +240,7 @@ int sort_candidate_blocks(int32_t* blocks, int64_t batch, int32_t k, const int32
     if (page_table_stride < (max_blocks + bpp - 1) / bpp) return TOPK_ERR_ARG;
     if (batch == 0) return TOPK_OK;
     if (blocks == nullptr || page_table == nullptr || out_pages == nullptr) return TOPK_ERR_ARG;
+    if (device_cus() <= 0) return TOPK_ERR_DEVICE;
     TableParams p{blocks, k, lengths, n_cols, page_table, page_table_stride, (int32_t)bpp, out_pages};
     void* args[] = {&p};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&block_table_kernel), dim3((uint32_t)batch),

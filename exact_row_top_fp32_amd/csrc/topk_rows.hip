@@ -1338,13 +1338,16 @@ const char* topk_status_string(int status) {
         case TOPK_OK: return "ok";
         case TOPK_ERR_ARG: return "invalid argument";
         case TOPK_ERR_K: return "k outside [1, 2048]";
-        case TOPK_ERR_ALIGN: return "scores must be 16-byte aligned with row_stride % 4 == 0";
+        case TOPK_ERR_ALIGN: return "misaligned buffer or row stride";
+        case TOPK_ERR_DEVICE: return "no gfx950 device is current";
         case TOPK_ERR_LAUNCH: return "kernel launch failed";
         default: return "unknown status";
     }
 }
 
 int32_t topk_max_capacity(void) { return kCapacity; }
+
+int32_t topk_short_capacity(void) { return kShortCapacity; }
 
 uint32_t topk_watchdog_trips(void) {
     unsigned int n = 0;
@@ -1360,28 +1363,35 @@ int topk_select_ex(const float* scores, int64_t batch, int64_t row_stride, int64
     if (batch < 0 || batch > INT32_MAX) return TOPK_ERR_ARG;
     if (k < 1 || k > TOPK_MAX_K) return TOPK_ERR_K;
     if (n_cols < 0 || n_cols > INT32_MAX || row_stride < n_cols) return TOPK_ERR_ARG;
-    topk_options opt{TOPK_PATH_AUTO, 0, nullptr};
+    topk_options opt{TOPK_PATH_AUTO, 0, nullptr, TOPK_KERNEL_AUTO};
     if (options != nullptr) opt = *options;
     if (opt.force_path < TOPK_PATH_AUTO || opt.force_path > TOPK_PATH_FULLROW) return TOPK_ERR_ARG;
     if (opt.capacity < 0 || opt.capacity > kCapacity) return TOPK_ERR_ARG;
-    if (opt.capacity == 0) opt.capacity = kCapacity;
+    if (opt.kernel < TOPK_KERNEL_AUTO || opt.kernel > TOPK_KERNEL_SHORT) return TOPK_ERR_ARG;
     if (page_table != nullptr) {
         if (page_size < 1) return TOPK_ERR_ARG;
         if (page_table_stride < (n_cols + page_size - 1) / page_size) return TOPK_ERR_ARG;
     }
+    // the kernel: one workgroup per row for batches of short rows (the
+    // hardware scheduler filling the compute units), else the persistent one;
+    // a capacity above what the short-row kernel holds needs the persistent one
+    int kernel = opt.kernel;
+    if (kernel == TOPK_KERNEL_AUTO)
+        kernel = n_cols <= kShortMaxCols && batch <= kShortMaxBatch && opt.capacity <= kShortCapacity
+                     ? TOPK_KERNEL_SHORT
+                     : TOPK_KERNEL_PERSISTENT;
+    if (kernel == TOPK_KERNEL_SHORT && (opt.capacity > kShortCapacity || batch > kShortMaxBatch)) return TOPK_ERR_ARG;
     if (batch == 0) return TOPK_OK;
     if (scores == nullptr || out_idx == nullptr) return TOPK_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(scores) & 15u) != 0) return TOPK_ERR_ALIGN;
     if (batch > 1 && (row_stride & 3) != 0) return TOPK_ERR_ALIGN;
-    // short rows on the automatic path: one workgroup per row, survivors in
-    // LDS, the hardware scheduler filling the compute units
-    if (n_cols <= kShortMaxCols && batch <= kShortMaxBatch && opt.force_path == TOPK_PATH_AUTO &&
-        opt.capacity == kCapacity && (options == nullptr || options->capacity == 0))
-        return launch_short_rows(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
-                                 page_table_stride, page_size, opt.row_stats, static_cast<hipStream_t>(hip_stream));
     const int cus = device_cus();
-    if (cus <= 0) return TOPK_ERR_LAUNCH;
+    if (cus <= 0) return TOPK_ERR_DEVICE;
+    if (kernel == TOPK_KERNEL_SHORT)
+        return launch_short_rows(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
+                                 page_table_stride, page_size, opt, static_cast<hipStream_t>(hip_stream));
 
+    if (opt.capacity == 0) opt.capacity = kCapacity;
     Params p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride, page_size, k,
              opt.force_path, opt.capacity, opt.row_stats, batch};
     void* args[] = {&p};

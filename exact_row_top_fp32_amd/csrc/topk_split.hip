@@ -190,6 +190,17 @@ struct SampleBinView {
     }
 };
 
+// A sample key the first histogram put in the bin [edge, top] (keys from lo
+// on), in sub-bins of width 2^sh from edge.
+struct SubBinView {
+    uint32_t edge, lo, top;
+    int sh;
+    __device__ bool operator()(uint32_t key, uint32_t, uint32_t& v) const {
+        v = (key - edge) >> sh;
+        return key >= lo && key <= top;
+    }
+};
+
 // The cutoff key of a row from its sample: `runs` runs of 64 contiguous
 // scores at evenly spaced offsets over [0, L). When the sample has fewer than
 // `want` keys above the row's m-th largest, fewer than m scores can be at or
@@ -198,15 +209,16 @@ struct SampleBinView {
 // mu = m n / L, and want = ceil(mu + 6 sqrt(mu) + 4). T is at or below the
 // want-th largest sample key: the lower edge of its bin in one histogram of
 // the keys in [lo, hi] (lo a bound from each lane's largest keys, hi the
-// largest below +inf's, bins a power of two wide), or, when the lanes hold
+// largest below +inf's, bins a power of two wide; a bin crowded below the
+// wanted key is split once more), or, when the lanes hold
 // too few keys for that bound, the lowest key of its top 22 bits (two 11-bit
 // digits, at most 2^10 keys below it).
 //
-// `issue` runs right after the sample's loads are issued (and on the early
-// return), so that a caller's own loads are in flight while the cutoff is
-// found.
+// `issue(true)` runs right after the sample's loads are issued (`issue(false)`
+// on the early return of a row too short to sample), so that a caller's own
+// loads are in flight while the cutoff is found.
 struct NoIssue {
-    __device__ void operator()() const {}
+    __device__ void operator()(bool) const {}
 };
 
 struct Cutoff {
@@ -221,7 +233,7 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
     const int64_t fit = L / (2 * kRunLen);
     const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
     if (runs < 2) {
-        issue();
+        issue(false);
         return Cutoff{0u, 0xFFFFFFFFu};
     }
     constexpr int kVecPerRun = kRunLen / E::kPerVec;
@@ -238,7 +250,7 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
         const int64_t start = ((int64_t)r * span / (runs - 1)) / E::kPerVec;
         if (t < nsv) x[h] = rv[start + t % kVecPerRun];
     }
-    issue();
+    issue(true);
     const uint32_t n = (uint32_t)(E::kPerVec * nsv);
     const float mu = (float)m * (float)n / (float)L;
     const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
@@ -298,7 +310,22 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
         while (((hi - lo) >> sh) >= (uint32_t)(kBins - 2)) ++sh;
         const uint32_t base = lo & ~((1u << sh) - 1u);  // (hi - base) >> sh <= kBins - 2
         const Cut c = radix_select<B>(lds, LdsKeys{skey, n}, SampleBinView{lo, hi, base, sh}, want, 0u, kDigitBits, n);
-        return Cutoff{c.value == (uint32_t)(kBins - 1) ? hi + 1u : base + (c.value << sh), shi};
+        if (c.value == (uint32_t)(kBins - 1)) return Cutoff{hi + 1u, shi};
+        const uint32_t edge = base + (c.value << sh);
+        // A few far keys (peaks well above a dense bulk) stretch [lo, hi] so
+        // that one bin can hold much of the bulk: a cutoff at its lower edge
+        // would let most of the row through and overflow the buffer. When
+        // the sample keys in the cutoff bin below the wanted one would add
+        // more than a quarter to the survivors, a second histogram of that
+        // bin alone, 2^10 times finer, places T.
+        if (sh > 0 && 4u * (c.equal - c.need) > want) {
+            const int sh2 = sh > kDigitBits - 1 ? sh - (kDigitBits - 1) : 0;
+            const uint32_t top = min(edge + ((1u << sh) - 1u), hi);  // no overflow: hi < +inf's key
+            const Cut c2 = radix_select<B>(lds, LdsKeys{skey, n}, SubBinView{edge, max(edge, lo), top, sh2},
+                                           c.need, 0u, kDigitBits, c.equal);
+            return Cutoff{edge + (c2.value << sh2), shi};
+        }
+        return Cutoff{edge, shi};
     }
     constexpr int kDropBits = 32 - 2 * kDigitBits;
     const uint32_t T =
@@ -583,7 +610,7 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
 // kShortMaxCols scores with k <= 2048 keep about 2900 survivors at most on
 // average (the sample's rank rule), so overflow needs a row far from its
 // sample's picture; it then takes the full-row selection.
-constexpr int kShortCap = 3840;
+constexpr int kShortCap = kShortCapacity;
 
 template <class E>
 __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) {
@@ -616,7 +643,18 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     B::sync();
     const SelectLds lds{hist, found};
     const typename E::Scalar* row = reinterpret_cast<const typename E::Scalar*>(p.scores) + b * p.row_stride;
-    const bool keep_all = L <= kShortCap;
+    // the row's path: the caller may force one (topk_options); otherwise
+    // rows up to the capacity keep every score and longer rows are sampled
+    const uint32_t cap = (uint32_t)p.capacity;  // 1 .. kShortCap
+    if (p.force_path == TOPK_PATH_FULLROW || (p.force_path == TOPK_PATH_LDS && L > (int64_t)cap)) {
+        const ElemRowSource<B, E> src{row, L};
+        const Selection s = select_top<B>(lds, src, m, (uint32_t)L, 0u, 0xFFFFFFFFu, bits_for(L));
+        OutRow out = split_out_row(p, b, m, &emitted);
+        emit(src, s, out);
+        if (threadIdx.x == 0) split_stats(p, b, TOPK_ROW_FULL_FORCED, (uint32_t)L);
+        return;
+    }
+    const bool keep_all = p.force_path != TOPK_PATH_SAMPLED && L <= (int64_t)cap;
 
     // one streaming pass, two rounds of loads in flight; hits go to LDS. A
     // sampled row's first two rounds are issued right behind the sample's
@@ -634,9 +672,12 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     // Every lane loads; a lane past the row's full loads takes the last one
     // again (the filter skips it). With a fixed number of loads issued after
     // the sample's, the sample can be used once its own loads are in, these
-    // still in flight. A sampled row has more than kShortCap scores, so
-    // nvec >= 1.
-    auto first_loads = [&]() {
+    // still in flight. A row with a sample has at least 2 * kRunLen * 2
+    // scores, so nvec >= 1 there; a row too short to sample (only when the
+    // sampled path is forced) may have no full load at all and then loads
+    // nothing.
+    auto first_loads = [&](bool sampled) {
+        if (!sampled && nvec == 0) return;
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t g = u * kThreads + threadIdx.x;
@@ -672,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
                 for (int j = 0; j < E::kPerVec; ++j) {
                     const uint32_t bits = E::bits(x[u], j);
                     if (g < nvec && elem_key<E>(bits) >= T) {
-                        if (slot < (uint32_t)kShortCap) buf[slot] = make_uint2(bits, (uint32_t)(E::kPerVec * g + j));
+                        if (slot < cap) buf[slot] = make_uint2(bits, (uint32_t)(E::kPerVec * g + j));
                         ++slot;
                     }
                 }
@@ -694,14 +735,14 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         const uint32_t bits = i < L ? E::scalar_bits(row[i]) : 0u;
         const bool hit = i < L && elem_key<E>(bits) >= T;
         const uint32_t slot = wave_reserve_count(&count, hit ? 1u : 0u);
-        if (hit && slot < (uint32_t)kShortCap) buf[slot] = make_uint2(bits, (uint32_t)i);
+        if (hit && slot < cap) buf[slot] = make_uint2(bits, (uint32_t)i);
     }
     B::sync();
     const uint32_t n = count;
     OutRow out = split_out_row(p, b, m, &emitted);
     int code;
-    if (n > (uint32_t)kShortCap || n < m) {
-        code = n > (uint32_t)kShortCap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
+    if (n > cap || n < m) {
+        code = n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
         const ElemRowSource<B, E> src{row, L};
         const Selection s = select_top<B>(lds, src, m, (uint32_t)L, 0u, 0xFFFFFFFFu, bits_for(L));
         emit(src, s, out);
@@ -719,10 +760,12 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
 template <class E>
 int launch_short(const void* scores, int64_t batch, int64_t row_stride, int64_t n_cols, const int32_t* lengths,
                  int32_t k, int32_t* out_idx, const int32_t* page_table, int64_t page_table_stride,
-                 int32_t page_size, int32_t* row_stats, hipStream_t stream) {
+                 int32_t page_size, const topk_options& opt, hipStream_t stream) {
     if (batch * kThreads > (int64_t)UINT32_MAX) return TOPK_ERR_ARG;
+    const int32_t cap = opt.capacity == 0 ? kShortCap : opt.capacity;
+    if (cap < 1 || cap > kShortCap) return TOPK_ERR_ARG;
     SplitParams p{static_cast<const float*>(scores), row_stride, n_cols, lengths, out_idx, page_table,
-                  page_table_stride, page_size, k, TOPK_PATH_AUTO, kShortCap, row_stats, batch, nullptr, nullptr, 0, 1};
+                  page_table_stride, page_size, k, opt.force_path, cap, opt.row_stats, batch, nullptr, nullptr, 0, 1};
     void* args[] = {&p};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&short_rows_kernel<E>), dim3((uint32_t)batch),
                                          dim3(kThreads), args, 0, stream);
@@ -731,16 +774,17 @@ int launch_short(const void* scores, int64_t batch, int64_t row_stride, int64_t 
 
 int launch_short_rows(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
                       const int32_t* lengths, int32_t k, int32_t* out_idx, const int32_t* page_table,
-                      int64_t page_table_stride, int32_t page_size, int32_t* row_stats, hipStream_t stream) {
+                      int64_t page_table_stride, int32_t page_size, const topk_options& opt, hipStream_t stream) {
     return launch_short<F32Elem>(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
-                                 page_table_stride, page_size, row_stats, stream);
+                                 page_table_stride, page_size, opt, stream);
 }
 
 int launch_short_rows_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
                            const int32_t* lengths, int32_t k, int32_t* out_idx, const int32_t* page_table,
-                           int64_t page_table_stride, int32_t page_size, hipStream_t stream) {
+                           int64_t page_table_stride, int32_t page_size, const topk_options& opt,
+                           hipStream_t stream) {
     return launch_short<Bf16Elem>(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
-                                  page_table_stride, page_size, nullptr, stream);
+                                  page_table_stride, page_size, opt, stream);
 }
 
 }  // namespace topk
@@ -765,10 +809,11 @@ int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, in
     if (k < 1 || k > TOPK_MAX_K) return TOPK_ERR_K;
     if (n_cols < 0 || n_cols > INT32_MAX || row_stride < n_cols) return TOPK_ERR_ARG;
     if (pieces < 0 || pieces > kMaxPieces) return TOPK_ERR_ARG;
-    topk_options opt{TOPK_PATH_AUTO, 0, nullptr};
+    topk_options opt{TOPK_PATH_AUTO, 0, nullptr, TOPK_KERNEL_AUTO};
     if (options != nullptr) opt = *options;
     if (opt.force_path < TOPK_PATH_AUTO || opt.force_path > TOPK_PATH_FULLROW) return TOPK_ERR_ARG;
     if (opt.capacity < 0 || opt.capacity > kSplitCapacity) return TOPK_ERR_ARG;
+    if (opt.kernel != TOPK_KERNEL_AUTO) return TOPK_ERR_ARG;  // the split kernels only
     if (opt.capacity == 0) opt.capacity = (int32_t)kSplitCapacity;
     if (page_table != nullptr) {
         if (page_size < 1) return TOPK_ERR_ARG;
@@ -785,7 +830,7 @@ int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, in
     int64_t want = pieces;
     if (want == 0) {
         const int cus = device_cus();
-        if (cus <= 0) return TOPK_ERR_LAUNCH;
+        if (cus <= 0) return TOPK_ERR_DEVICE;
         want = (4 * (int64_t)cus + batch - 1) / batch;
     }
     const int64_t nvec_max = (n_cols + 3) / 4;
@@ -796,6 +841,7 @@ int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, in
     if (per < kRound) per = kRound;
     const int64_t P = nvec_max > 0 ? (nvec_max + per - 1) / per : 1;
     if (batch * P * kThreads > (int64_t)UINT32_MAX) return TOPK_ERR_ARG;
+    if (device_cus() <= 0) return TOPK_ERR_DEVICE;
 
     char* ws = static_cast<char*>(workspace);
     SplitParams p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride, page_size, k,

@@ -60,7 +60,9 @@ extern "C" {
                              page_size < 1 or page_table_stride too small, bad option value */
 #define TOPK_ERR_K 2      /* k outside [1, TOPK_MAX_K] */
 #define TOPK_ERR_ALIGN 3  /* scores not 16-byte aligned, or row_stride % 4 != 0 with batch > 1 */
-#define TOPK_ERR_LAUNCH 5 /* the HIP launch itself failed (e.g. no gfx950 device) */
+#define TOPK_ERR_DEVICE 4 /* no device is current, or the current one is not a gfx950 (the
+                             library holds gfx950 code only); pointers are not inspected */
+#define TOPK_ERR_LAUNCH 5 /* the HIP launch itself failed */
 
 #define TOPK_MAX_K 2048
 
@@ -69,6 +71,11 @@ extern "C" {
 #define TOPK_PATH_LDS 1      /* every position kept in LDS, exact select there (rows <= capacity) */
 #define TOPK_PATH_SAMPLED 2  /* sampled cutoff, one streaming pass, exact select on survivors */
 #define TOPK_PATH_FULLROW 3  /* full-row exact: histogram-only passes, one emission pass */
+
+/* kernels (for topk_options.kernel) */
+#define TOPK_KERNEL_AUTO 0        /* topk_select's choice (see topk_select_ex) */
+#define TOPK_KERNEL_PERSISTENT 1  /* one workgroup per compute unit, rows in turn */
+#define TOPK_KERNEL_SHORT 2       /* one workgroup per row, survivors in LDS */
 
 /* row statistics codes, written to row_stats[2*b] */
 #define TOPK_ROW_EMPTY 0          /* m == 0: every slot -1 */
@@ -95,7 +102,8 @@ extern "C" {
  *  page_table_stride  elements between page-table rows, >= ceil(n_cols / page_size)
  *  page_size          positions per page, >= 1 when page_table is given
  *  hip_stream         hipStream_t to launch on
- * Returns TOPK_OK or an error code; on error nothing was launched.
+ * Returns TOPK_OK or an error code (TOPK_ERR_ARG, TOPK_ERR_K, TOPK_ERR_ALIGN,
+ * TOPK_ERR_DEVICE, TOPK_ERR_LAUNCH); on error nothing was launched.
  * The caller keeps slot values inside int32 (page * page_size + offset).
  */
 int topk_select(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
@@ -106,19 +114,33 @@ int topk_select(const float* scores, int64_t batch, int64_t row_stride, int64_t 
 /*
  * Diagnostic and test controls for topk_select_ex. A zeroed struct (or a NULL
  * pointer) gives exactly topk_select. The selected set never depends on them:
- * every path returns the same unique set.
+ * every path of every kernel returns the same unique set, so they exist to
+ * reach each path on chosen rows (the forced-backend audit of the vLLM PR
+ * #56346 report, discussion).
  *  force_path  TOPK_PATH_* for every row with k < L (rows with L <= k take the
  *              direct path); LDS forced on a row longer than the capacity runs
- *              the full-row path instead
- *  capacity    survivor capacity in entries, 1..topk_max_capacity() (0 = maximum);
- *              a small value makes the overflow fallback easy to reach
+ *              the full-row path instead (row code TOPK_ROW_FULL_FORCED);
+ *              SAMPLED forced on a row too short to sample (fewer than 256
+ *              scores) keeps every score under a cutoff of 0
+ *  capacity    survivor capacity in entries (0 = the kernel's maximum):
+ *              1..topk_max_capacity() for the persistent kernel,
+ *              1..topk_short_capacity() for the short-row kernel; a small
+ *              value makes the overflow fallback easy to reach, and rows of
+ *              at most `capacity` scores keep every score on the automatic path
  *  row_stats   device int32 [batch, 2] or NULL: [2b] = TOPK_ROW_* code,
  *              [2b+1] = survivors of the streaming pass (or L on the other paths)
+ *  kernel      TOPK_KERNEL_*: AUTO takes the short-row kernel when
+ *              n_cols <= 32768 and capacity <= topk_short_capacity(), else the
+ *              persistent kernel; SHORT with a capacity above
+ *              topk_short_capacity() is TOPK_ERR_ARG. Either kernel takes any
+ *              width; the short-row kernel sends rows whose survivors
+ *              overflow its buffer to the full-row path.
  */
 typedef struct topk_options {
     int32_t force_path;
     int32_t capacity;
     int32_t* row_stats;
+    int32_t kernel;
 } topk_options;
 
 int topk_select_ex(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
@@ -129,8 +151,13 @@ int topk_select_ex(const float* scores, int64_t batch, int64_t row_stride, int64
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* topk_status_string(int status);
 
-/* Largest survivor capacity (entries held in one LDS buffer). */
+/* Largest survivor capacity of the persistent kernel (entries held in one
+ * LDS buffer). */
 int32_t topk_max_capacity(void);
+
+/* Largest survivor capacity of the short-row kernel (entries held in LDS per
+ * row). */
+int32_t topk_short_capacity(void);
 
 /*
  * Workgroups that gave up a wait between their roles since the library was
@@ -166,7 +193,8 @@ uint32_t topk_watchdog_trips(void);
  *                   whole number of 8192-score rounds, so short rows get
  *                   fewer pieces
  *  options          as for topk_select_ex, with capacity up to
- *                   topk_split_capacity(); TOPK_PATH_LDS keeps every score of
+ *                   topk_split_capacity() and kernel TOPK_KERNEL_AUTO (this
+ *                   entry has its own kernels); TOPK_PATH_LDS keeps every score of
  *                   rows up to the capacity (others take the full-row path);
  *                   row_stats codes as for topk_select_ex (TOPK_ROW_LDS: every
  *                   score was kept). NULL = automatic.
@@ -208,8 +236,20 @@ int topk_select_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, 
                      void* hip_stream);
 
 /*
- * Level-one keys of the two-level indexer (same page, implementation section
- * 2, block-max kernel, and the amax8_varlen docstring in the code excerpts).
+ * topk_select_bf16 with the diagnostic controls of topk_select_ex (the same
+ * audit: every path of the bf16 kernel reached on chosen rows). kernel must
+ * be TOPK_KERNEL_AUTO or TOPK_KERNEL_SHORT (bf16 rows have only the short-row
+ * kernel); capacity up to topk_short_capacity(). Same result for any options.
+ */
+int topk_select_bf16_ex(const uint16_t* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                        const int32_t* lengths, int32_t k, int32_t* out_idx,
+                        const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                        void* hip_stream, const topk_options* options);
+
+/*
+ * Block keys for the first stage of the two-level indexer (same page,
+ * implementation section 2, the block-max kernel, and its amax8_varlen entry
+ * among the code excerpts, whose name and argument order are kept).
  * For row b with L = clamp(lengths[b], 0, n_cols) and nb = ceil(L / 8):
  * out[b, i] = the largest of scores[b, 8i .. 8i+7] for i < nb - 1, NaN
  * ignored and +0 above -0 (a block of NaN only gives +qNaN 0x7FC00000);
@@ -223,16 +263,19 @@ int topk_select_bf16(const uint16_t* scores, int64_t batch, int64_t row_stride, 
  *  out         fp32 [batch, out_stride], out_stride >= ceil(n_cols / 8);
  *              device memory owned by the caller
  * Returns TOPK_OK, TOPK_ERR_ARG (sizes, topk < 0, NULL, out_stride too
- * small), TOPK_ERR_ALIGN or TOPK_ERR_LAUNCH. Asynchronous on hip_stream.
+ * small), TOPK_ERR_ALIGN, TOPK_ERR_DEVICE or TOPK_ERR_LAUNCH. Asynchronous
+ * on hip_stream.
  */
 int amax8_varlen(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
                  const int32_t* lengths, int32_t topk, float* out, int64_t out_stride,
                  void* hip_stream);
 
 /*
- * The candidate block table (same page, implementation section 2, candidate
- * block table kernel, and the sort_candidate_blocks docstring). For row b with
- * nb = ceil(clamp(lengths[b], 0, n_cols) / 8):
+ * Block table for the second stage of the two-level indexer (same page,
+ * implementation section 2, the candidate-block-table kernel, and its
+ * sort_candidate_blocks entry among the code excerpts). For row b with
+ * nb = ceil(clamp(lengths[b], 0, n_cols) / 8) (a length past n_cols counts as
+ * n_cols, as everywhere in this library):
  *  - nb <= k: blocks[b] becomes 0 .. nb-1, then INT32_MAX (input unread);
  *  - otherwise: the distinct ids among blocks[b, 0..k) that lie in [0, nb),
  *    ascending, then INT32_MAX (a top-k selection gives k distinct ids);
@@ -245,8 +288,8 @@ int amax8_varlen(const float* scores, int64_t batch, int64_t row_stride, int64_t
  *                     page_table_stride >= ceil(ceil(n_cols / 8) / bpp)
  *  page_size          a power of two, at least 8
  *  out_pages          int32 [batch, k] contiguous
- * Returns TOPK_OK, TOPK_ERR_ARG or TOPK_ERR_LAUNCH. Asynchronous on
- * hip_stream. The caller keeps pool slots inside int32.
+ * Returns TOPK_OK, TOPK_ERR_ARG, TOPK_ERR_DEVICE or TOPK_ERR_LAUNCH.
+ * Asynchronous on hip_stream. The caller keeps pool slots inside int32.
  */
 int sort_candidate_blocks(int32_t* blocks, int64_t batch, int32_t k, const int32_t* lengths,
                           int64_t n_cols, const int32_t* page_table, int64_t page_table_stride,

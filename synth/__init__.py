@@ -227,6 +227,46 @@ def mixed_rows(kinds, W: int, k: int, seed: int, *, row_stride: int | None = Non
     return Workload(name, seed, scores, lengths, W, k, kinds=list(kinds))
 
 
+def cutoff_group_rows(group: int, kind: str, batch: int = 4, width: int = 16384, k: int = 512,
+                      seed: int = 43) -> Workload:
+    """Rows whose k-th largest score falls inside a group of ``group`` scores
+    that nothing else comes near: k - 17 distinct scores well above it, the
+    group, and a background well below, so 17 of the group are selected.
+    ``kind`` "ties": the group is one value repeated; "cluster": the group is
+    ``group`` consecutive fp32 patterns (distinct values closer together than
+    any coarse bin). Even rows: N(0,1) background, the group at +32, the
+    scores above from +64 up; odd rows: background below -2, the group at -1,
+    the scores above from +1 up. Every fourth row pair is ragged. (The exact
+    capacity boundaries the sparse-attention top-k fix thread found bugs at,
+    applied to each finisher's direct-ranking limit.)"""
+    rng = _rng(seed, group, zlib.crc32(kind.encode()))
+    above = k - 17
+    scores = np.empty((batch, width), np.float32)
+    lengths = np.full(batch, width, np.int32)
+    for b in range(batch):
+        if b % 2 == 0:
+            row = np.clip(rng.standard_normal(width, dtype=np.float32), -31.0, 31.0)
+            g0, top0 = 0x42000000, 0x42800000
+        else:
+            row = (-2.0 - np.abs(rng.standard_normal(width))).astype(np.float32)
+            g0, top0 = 0xBF800000, 0x3F800000
+        if b % 4 >= 2:
+            lengths[b] = width - 1 - int(rng.integers(0, 64))
+        L = int(lengths[b])
+        pos = rng.permutation(L)[:above + group]
+        row[pos[:above]] = _from_bits(top0 + (np.arange(above, dtype=np.uint32) << np.uint32(16)))
+        if kind == "ties":
+            g = np.full(group, g0, np.uint32)
+        elif kind == "cluster":  # consecutive patterns; for the negative group larger bits are smaller values
+            g = g0 + np.arange(group, dtype=np.uint32)
+        else:
+            raise ValueError(kind)
+        row[pos[above:]] = _from_bits(g)
+        scores[b] = row
+    poison_tails(scores, lengths)
+    return Workload(f"group{group}_{kind}_{batch}x{width}", seed, scores, lengths, width, k)
+
+
 # ----------------------------------------------------------------------------
 # the five named workloads
 # ----------------------------------------------------------------------------

@@ -24,7 +24,7 @@ ARGS = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.
 
 class Options(ctypes.Structure):
     _fields_ = [("force_path", ctypes.c_int32), ("capacity", ctypes.c_int32),
-                ("row_stats", ctypes.c_void_p)]
+                ("row_stats", ctypes.c_void_p), ("kernel", ctypes.c_int32)]
 
 
 def header_functions():
@@ -61,8 +61,9 @@ def lib():
 def test_header_declares_the_entry_points():
     assert header_functions() == sorted(
         ["topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity",
-         "topk_watchdog_trips", "topk_select_split", "topk_split_workspace_bytes",
-         "topk_split_capacity", "topk_select_bf16", "amax8_varlen", "sort_candidate_blocks"])
+         "topk_short_capacity", "topk_watchdog_trips", "topk_select_split", "topk_split_workspace_bytes",
+         "topk_split_capacity", "topk_select_bf16", "topk_select_bf16_ex", "amax8_varlen",
+         "sort_candidate_blocks"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -103,6 +104,12 @@ def test_host_argument_checks(lib):
     assert call(lib, opt=Options(7, 0, None)) == 1
     assert call(lib, opt=Options(0, lib.topk_max_capacity() + 1, None)) == 1
     assert call(lib, opt=Options(0, -1, None)) == 1
+    # kernel choice: values, and a capacity the short-row kernel cannot hold
+    lib.topk_short_capacity.restype = ctypes.c_int32
+    short_cap = lib.topk_short_capacity()
+    assert 0 < short_cap < lib.topk_max_capacity()
+    assert call(lib, opt=Options(0, 0, None, 3)) == 1 and call(lib, opt=Options(0, 0, None, -1)) == 1
+    assert call(lib, opt=Options(0, short_cap + 1, None, 2)) == 1
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -111,7 +118,7 @@ def test_empty_batch_is_a_no_op(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, 1, 2, 3, 5, 99):
+    for code in (0, 1, 2, 3, 4, 5, 99):
         assert lib.topk_status_string(code)
     assert lib.topk_max_capacity() >= 4096
 
@@ -153,6 +160,7 @@ def test_split_host_argument_checks(lib):
     assert split_call(lib, page_table=FAKE, page_size=0, pt_stride=64) == 1
     assert split_call(lib, opt=Options(4, 0, None)) == 1
     assert split_call(lib, opt=Options(0, lib.topk_split_capacity() + 1, None)) == 1
+    assert split_call(lib, opt=Options(0, 0, None, 1)) == 1  # the split entry has its own kernels
     # a grid past 2^32 work-items
     assert split_call(lib, batch=2**24, n_cols=2**31 - 1, row_stride=2**31, ws_bytes=2**62,
                       pieces=256) == 1
@@ -206,3 +214,20 @@ def test_binding_rejects_narrow_page_tables():
     blocks = torch.zeros((4, 8), dtype=torch.int32)
     with pytest.raises(ValueError, match="page_table"):  # 1000 positions: 125 blocks, 16 pages of 8
         topk.sort_candidate_blocks(blocks, None, pt, 64, n_cols=1000)
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present: the call would launch")
+def test_valid_calls_without_a_device_return_device_error(lib):
+    # every argument valid, but no gfx950 device is current: TOPK_ERR_DEVICE
+    # before any launch (the pointers are never used)
+    assert call(lib) == 4
+    assert call(lib, opt=Options(2, 100, None, 1)) == 4
+    assert call(lib, n_cols=40000, row_stride=40000) == 4
+    assert split_call(lib) == 4
+    lib.topk_select_bf16.argtypes = ARGS
+    assert lib.topk_select_bf16(FAKE, 4, 1024, 1024, None, 16, FAKE, None, 0, 0, None) == 4
+    lib.topk_select_bf16_ex.argtypes = ARGS + [ctypes.POINTER(Options)]
+    assert lib.topk_select_bf16_ex(FAKE, 4, 1024, 1024, None, 16, FAKE, None, 0, 0, None,
+                                   ctypes.byref(Options(1, 0, None, 1))) == 1  # no persistent bf16 kernel
+    assert lib.topk_select_bf16_ex(FAKE, 4, 1024, 1024, None, 16, FAKE, None, 0, 0, None,
+                                   ctypes.byref(Options(3, 0, None, 2))) == 4

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from topk_check import check
+from topk_check import check, check_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,37 @@ def test_bf16_length_boundaries(topk):
     synth.poison_tails_bf16(bits, np.clip(lens, 0, W))
     wl = synth.Bf16Workload("bf16_lengths", 64, bits, lens, W, k)
     bf16_parity(wl, run_bf16(topk, wl))
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+@pytest.mark.parametrize("force", [0, 1, 2, 3], ids=["auto", "lds", "sampled", "fullrow"])
+def test_bf16_forced_paths(topk, force, k):
+    # every path of the bf16 kernel on the adversarial rows and on rows whose
+    # lengths sit at k, the LDS capacity and the width, with the path code of
+    # every row checked; the default capacity, then a small one
+    cap = topk.topk_short_capacity()
+    adv = synth.bf16_adversarial(k)
+    W = 16384
+    lens = np.array([-1, 0, 1, k - 1, k, k + 1, cap - 1, cap, cap + 1, 2 * cap, W - 1, W, W + 17], np.int32)
+    rng = np.random.default_rng(72 + k)
+    bits = synth.to_bf16_bits(rng.standard_normal((lens.size, W)).astype(np.float32))
+    synth.poison_tails_bf16(bits, np.clip(lens, 0, W))
+    edges = synth.Bf16Workload("bf16_length_edges", 72, bits, lens, W, k)
+    for wl in (adv, edges):
+        for capacity in (0, 700):
+            ln = torch.from_numpy(np.ascontiguousarray(wl.lengths)).cuda()
+            s = torch.from_numpy(wl.bits.view(np.int16)).cuda().view(torch.bfloat16)
+            pt = torch.from_numpy(wl.page_table).cuda() if wl.page_table is not None else None
+            buf, out = guarded((wl.batch, k), torch.int32, CANARY)
+            stats = torch.full((wl.batch, 2), -7, dtype=torch.int32, device="cuda")
+            say(f"  gpu bf16 call: {wl.name} k={k} force={force} cap={capacity}")
+            topk.topk_select_bf16_ex(s, ln, k, out, pt, wl.page_size, n_cols=wl.n_cols, force_path=force,
+                                     capacity=capacity, row_stats=stats)
+            torch.cuda.synchronize()
+            assert guards_intact(buf, CANARY), "write outside out"
+            bf16_parity(wl, out.cpu().numpy(), k=k)
+            fails = check_codes(stats.cpu().numpy(), wl.lengths, wl.n_cols, k, force, capacity or cap)
+            assert not fails, "\n".join(fails[:10])
 
 
 def test_bf16_single_row_odd_width(topk):

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import synth
-from topk_check import check, check_fast_raw
+from topk_check import check, check_codes, check_fast_raw
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def say(*msg):
 
 
 def run(topk, wl, *, k=None, force=0, capacity=0, lengths=None, scores_dev=None,
-        n_cols=None, want_stats=False):
+        n_cols=None, want_stats=False, kernel=0):
     """Launch through the C ABI with guarded output; returns (out, stats)."""
     k = wl.k if k is None else k
     B = wl.batch
@@ -57,9 +57,9 @@ def run(topk, wl, *, k=None, force=0, capacity=0, lengths=None, scores_dev=None,
     buf = torch.full((B * k + 2 * GUARD,), CANARY, dtype=torch.int32, device="cuda")
     out = buf[GUARD:GUARD + B * k].view(B, k)
     stats = torch.full((B, 2), -7, dtype=torch.int32, device="cuda") if want_stats else None
-    say(f"  gpu call: {wl.name} k={k} force={force} cap={capacity}")
+    say(f"  gpu call: {wl.name} k={k} force={force} cap={capacity} kernel={kernel}")
     topk.topk_select_ex(s, ln, k, out, pt, wl.page_size, n_cols=n_cols or wl.n_cols,
-                        force_path=force, capacity=capacity, row_stats=stats)
+                        force_path=force, capacity=capacity, row_stats=stats, kernel=kernel)
     torch.cuda.synchronize()
     assert topk.topk_watchdog_trips() == 0, "a workgroup gave up waiting"
     h = buf.cpu().numpy()
@@ -82,6 +82,23 @@ def assert_parity(wl, got, want, k=None, lengths=None, n_cols=None):
 
 PATHS = [0, 1, 2, 3]
 PATH_IDS = ["auto", "lds", "sampled", "fullrow"]
+# topk_options.kernel: the automatic choice (the short-row kernel for widths
+# up to 32768), and the persistent kernel forced
+KERNELS = [0, 1]
+KERNEL_IDS = ["auto_kernel", "persistent"]
+
+
+def kernel_capacity(topk, kernel, n_cols, capacity=0):
+    """The survivor capacity the chosen kernel runs with."""
+    if capacity:
+        return capacity
+    short = kernel == 2 or (kernel == 0 and n_cols <= 32768)
+    return topk.topk_short_capacity() if short else topk.topk_max_capacity()
+
+
+def assert_codes(stats, lengths, n_cols, k, force, cap):
+    fails = check_codes(stats, lengths, n_cols, k, force, cap)
+    assert not fails, "\n".join(fails[:10])
 
 
 # ----------------------------------------------------------------------------
@@ -93,10 +110,12 @@ def c1():
     return synth.c1()
 
 
+@pytest.mark.parametrize("kernel", KERNELS, ids=KERNEL_IDS)
 @pytest.mark.parametrize("force", PATHS, ids=PATH_IDS)
-def test_c1_every_path(topk, c1, force):
-    got, stats = run(topk, c1, force=force, want_stats=True)
+def test_c1_every_path(topk, c1, force, kernel):
+    got, stats = run(topk, c1, force=force, want_stats=True, kernel=kernel)
     assert_parity(c1, got, expect(c1))
+    assert_codes(stats, c1.lengths, c1.n_cols, c1.k, force, kernel_capacity(topk, kernel, c1.n_cols))
 
 
 @pytest.fixture(scope="session", params=[512, 1024, 2048])
@@ -104,17 +123,19 @@ def c2(request):
     return synth.c2(request.param)
 
 
+@pytest.mark.parametrize("kernel", KERNELS, ids=KERNEL_IDS)
 @pytest.mark.parametrize("force", PATHS, ids=PATH_IDS)
-def test_c2_adversarial_every_path(topk, c2, force):
-    got, stats = run(topk, c2, force=force, want_stats=True)
+def test_c2_adversarial_every_path(topk, c2, force, kernel):
+    got, stats = run(topk, c2, force=force, want_stats=True, kernel=kernel)
     want = expect(c2)
     assert_parity(c2, got, want)
-    if force == 0:
-        say("  row paths:", dict(zip(*np.unique(stats[:, 0], return_counts=True))))
+    assert_codes(stats, c2.lengths, c2.n_cols, c2.k, force, kernel_capacity(topk, kernel, c2.n_cols))
+    say("  row paths:", dict(zip(*np.unique(stats[:, 0], return_counts=True))))
 
 
-def test_c2_small_capacity_forces_overflow(topk, c2):
-    got, stats = run(topk, c2, force=2, capacity=300, want_stats=True)
+@pytest.mark.parametrize("kernel", KERNELS, ids=KERNEL_IDS)
+def test_c2_small_capacity_forces_overflow(topk, c2, kernel):
+    got, stats = run(topk, c2, force=2, capacity=300, want_stats=True, kernel=kernel)
     assert_parity(c2, got, expect(c2))
     assert np.all(stats[:, 0] >= 4), "every row must fall back when m exceeds the capacity"
 
@@ -148,12 +169,14 @@ def test_c3_rows_forced_paths(topk, c3, force):
     assert not check_fast_raw(got, expect(sub), sub.lengths, sub.n_cols, sub.k)
 
 
+@pytest.mark.parametrize("kernel", [0, 2], ids=["auto_kernel", "short_rows"])
 @pytest.mark.parametrize("global_pool", [False, True], ids=["row_perm", "global_pool"])
 @pytest.mark.parametrize("force", PATHS, ids=PATH_IDS)
-def test_c5_paged(topk, force, global_pool):
+def test_c5_paged(topk, force, global_pool, kernel):
     wl = synth.c5(global_pool=global_pool)
-    got, _ = run(topk, wl, force=force)
+    got, stats = run(topk, wl, force=force, want_stats=True, kernel=kernel)
     assert_parity(wl, got, expect(wl))
+    assert_codes(stats, wl.lengths, wl.n_cols, wl.k, force, kernel_capacity(topk, kernel, wl.n_cols))
 
 
 # ----------------------------------------------------------------------------
@@ -167,9 +190,11 @@ def test_length_boundaries(topk):
     wl = synth.mixed_rows(["normal"] * len(lens), W, k, seed=21)
     wl.lengths = np.array(lens, np.int32)
     synth.poison_tails(wl.scores, np.clip(wl.lengths, 0, W))
-    for force in PATHS:
-        got, stats = run(topk, wl, force=force, want_stats=True)
-        assert_parity(wl, got, expect(wl))
+    for kernel in (0, 1):
+        for force in PATHS:
+            got, stats = run(topk, wl, force=force, want_stats=True, kernel=kernel)
+            assert_parity(wl, got, expect(wl))
+            assert_codes(stats, wl.lengths, W, k, force, kernel_capacity(topk, kernel, W))
 
 
 @pytest.mark.parametrize("k", [1, 2, 63, 64, 65, 2047, 2048])
@@ -177,9 +202,11 @@ def test_k_range(topk, k):
     wl = synth.mixed_rows(["normal", "heavy_ties", "constant", "signed_zero", "ascending"], 9000, k, seed=22)
     wl.lengths = np.array([9000, 9000, 2048, 2049, 5000], np.int32)
     synth.poison_tails(wl.scores, wl.lengths)
-    for force in PATHS:
-        got, _ = run(topk, wl, k=k, force=force)
-        assert_parity(wl, got, expect(wl, k=k), k=k)
+    for kernel in (0, 1):
+        for force in PATHS:
+            got, stats = run(topk, wl, k=k, force=force, want_stats=True, kernel=kernel)
+            assert_parity(wl, got, expect(wl, k=k), k=k)
+            assert_codes(stats, wl.lengths, wl.n_cols, k, force, kernel_capacity(topk, kernel, wl.n_cols))
 
 
 def test_offset_view_and_stride(topk):
@@ -221,12 +248,13 @@ def test_exact_capacity_boundary(topk):
             assert_parity(row, got, want[b:b + 1])
 
 
-def test_lds_capacity_boundary(topk):
+@pytest.mark.parametrize("kernel", [1, 2], ids=["persistent", "short_rows"])
+def test_lds_capacity_boundary(topk, kernel):
     cap = 3000
     wl = synth.mixed_rows(["normal", "heavy_ties", "normal", "heavy_ties"], 4000, 256, seed=26)
     wl.lengths = np.array([cap, cap, cap + 1, cap + 1], np.int32)
     synth.poison_tails(wl.scores, wl.lengths)
-    got, stats = run(topk, wl, capacity=cap, want_stats=True)
+    got, stats = run(topk, wl, capacity=cap, want_stats=True, kernel=kernel)
     assert list(stats[:, 0]) == [2, 2, stats[2, 0], stats[3, 0]] and stats[2, 0] >= 3
     assert_parity(wl, got, expect(wl))
 

@@ -93,3 +93,28 @@ def check_fast_raw(got, want, lengths, n_cols, k):
     same = np.all(np.sort(got, axis=1) == np.sort(want, axis=1), axis=1)
     bad = np.flatnonzero(~(a1 & same))
     return [int(b) for b in bad]
+
+
+def check_codes(stats, lengths, n_cols, k, force, cap):
+    """Each row's path code (row_stats[b, 0]) is one its forced path allows:
+    direct rows (L <= k) 0, or 1 when L > 0; full-row forced 6; LDS forced 2
+    up to the capacity, else 6; sampled 3, or 4/5 after an overflow or
+    underflow fallback; automatic 2 up to the capacity, else 3/4/5. The
+    second word is L wherever no stream ran. Returns the failures."""
+    fails = []
+    L = np.clip(np.asarray(lengths, np.int64), 0, n_cols)
+    for b in range(L.size):
+        code, seen = int(stats[b, 0]), int(stats[b, 1])
+        if L[b] <= k:
+            ok = {0 if L[b] == 0 else 1}
+        elif force == 3 or (force == 1 and L[b] > cap):
+            ok = {6}
+        elif force == 1 or (force == 0 and L[b] <= cap):
+            ok = {2}
+        else:
+            ok = {3, 4, 5}
+        if code not in ok:
+            fails.append(f"row {b}: L={L[b]} force={force} cap={cap}: code {code}, allowed {sorted(ok)}")
+        elif code in (0, 1, 2, 6) and seen != L[b]:
+            fails.append(f"row {b}: code {code} reports {seen}, L={L[b]}")
+    return fails

@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "topk_select", "topk_select_ex", "topk_select_split", "topk_split_workspace_bytes",
-    "topk_split_capacity", "topk_select_bf16", "amax8_varlen", "sort_candidate_blocks",
+    "topk_split_capacity", "topk_select_split_noalloc", "SPLIT_NOALLOC_MAX_BATCH", "topk_select_bf16",
+    "amax8_varlen", "sort_candidate_blocks",
     "topk_select_bf16_ex", "topk_status_string", "topk_max_capacity", "topk_short_capacity",
     "topk_watchdog_trips", "KERNEL_AUTO", "KERNEL_PERSISTENT", "KERNEL_SHORT",
     "TopKError", "library_path", "PATH_AUTO", "PATH_LDS", "PATH_SAMPLED", "PATH_FULLROW",
@@ -29,6 +30,7 @@ library_path = os.path.join(_PKG, "libexact_topk.so")
 MAX_K = 2048
 PATH_AUTO, PATH_LDS, PATH_SAMPLED, PATH_FULLROW = 0, 1, 2, 3
 KERNEL_AUTO, KERNEL_PERSISTENT, KERNEL_SHORT = 0, 1, 2
+SPLIT_NOALLOC_MAX_BATCH = 256
 (ROW_EMPTY, ROW_ALL, ROW_LDS, ROW_SAMPLED, ROW_FULL_OVERFLOW, ROW_FULL_UNDERFLOW,
  ROW_FULL_FORCED) = range(7)
 
@@ -72,6 +74,9 @@ def _load():
         lib.topk_select_split.restype = ctypes.c_int
         lib.topk_select_split.argtypes = (_ARGS[:-1] + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                                          ctypes.c_void_p, ctypes.POINTER(_Options)])
+        lib.topk_select_split_noalloc.restype = ctypes.c_int
+        lib.topk_select_split_noalloc.argtypes = (_ARGS[:-1] + [ctypes.c_int32, ctypes.c_void_p,
+                                                                 ctypes.POINTER(_Options)])
         lib.topk_split_workspace_bytes.restype = ctypes.c_int64
         lib.topk_split_workspace_bytes.argtypes = [ctypes.c_int64]
         lib.topk_split_capacity.restype = ctypes.c_int32
@@ -243,6 +248,24 @@ def topk_select_split(scores: torch.Tensor, lengths: torch.Tensor | None, k: int
     status = _load().topk_select_split(*args[:-1], _device_ptr(workspace, "workspace", torch.uint8),
                                        workspace.numel(), int(pieces), args[-1], ctypes.byref(opt))
     _check(status)
+    return out
+
+
+def topk_select_split_noalloc(scores: torch.Tensor, lengths: torch.Tensor | None, k: int,
+                              out: torch.Tensor, page_table: torch.Tensor | None = None,
+                              page_size: int = 0, *, pieces: int = 0, n_cols: int | None = None,
+                              stream=None, force_path: int = PATH_AUTO, capacity: int = 0,
+                              row_stats: torch.Tensor | None = None) -> torch.Tensor:
+    """``topk_select_split`` with its workspace in a fixed device array inside
+    the library (at most ``SPLIT_NOALLOC_MAX_BATCH`` rows): neither the
+    library nor this binding allocates device memory, so ``out`` must be
+    given. Calls that can overlap in time on one GPU share the array and race.
+    """
+    if out is None:
+        raise ValueError("out must be given: this entry allocates nothing")
+    args, out = _marshal(scores, lengths, k, out, page_table, page_size, n_cols, stream)
+    opt = _options(scores, force_path, capacity, row_stats, KERNEL_AUTO)
+    _check(_load().topk_select_split_noalloc(*args[:-1], int(pieces), args[-1], ctypes.byref(opt)))
     return out
 
 

@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "exact_topk.h"
 #include "topk_device.h"
 #include "topk_short.h"
@@ -89,7 +91,10 @@ struct SplitParams {
 
 constexpr int64_t kSplitCapacity = 8192;  // survivor entries per row in the workspace
 
-int64_t head_bytes(int64_t batch) { return (batch * (int64_t)sizeof(SplitHead) + 255) & ~(int64_t)255; }
+constexpr int64_t head_bytes(int64_t batch) { return (batch * (int64_t)sizeof(SplitHead) + 255) & ~(int64_t)255; }
+constexpr int64_t split_workspace_bytes(int64_t batch) {
+    return head_bytes(batch) + batch * kSplitCapacity * (int64_t)sizeof(uint2);
+}
 
 __device__ __forceinline__ int64_t split_row_len(const SplitParams& p, int64_t b) {
     int64_t L = p.lengths ? (int64_t)p.lengths[b] : p.n_cols;
@@ -787,25 +792,41 @@ int launch_short_rows_bf16(const uint16_t* scores, int64_t batch, int64_t row_st
                                   page_table_stride, page_size, opt, stream);
 }
 
-}  // namespace topk
+// The workspace of topk_select_split_noalloc: a fixed device array, one copy
+// per GPU, held until the process ends. Host code never names it except to
+// ask for its device address (the name is only a host-side stand-in).
+constexpr int64_t kNoAllocBytes = split_workspace_bytes(TOPK_SPLIT_NOALLOC_MAX_BATCH);
+static_assert(kNoAllocBytes % 256 == 0, "whole 256-byte lines");
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
 
-using namespace topk;
-
-extern "C" {
-
-int64_t topk_split_workspace_bytes(int64_t batch) {
-    if (batch < 0 || batch > INT32_MAX) return -1;
-    return head_bytes(batch) + batch * kSplitCapacity * (int64_t)sizeof(uint2);
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current; TOPK_ERR_DEVICE if no gfx950 device is
+// current or the lookup fails.
+int scratch_address(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static void* addr[kMaxDevices];
+    static hipError_t rc[kMaxDevices];
+    int dev = -1;
+    if (device_cus() <= 0 || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return TOPK_ERR_DEVICE;
+    std::call_once(once[dev], [dev] {
+        void* p = nullptr;
+        rc[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        addr[dev] = p;
+    });
+    if (rc[dev] != hipSuccess || addr[dev] == nullptr) return TOPK_ERR_DEVICE;
+    *ptr = addr[dev];
+    return TOPK_OK;
 }
 
-int32_t topk_split_capacity(void) { return (int32_t)kSplitCapacity; }
-
-int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
-                      const int32_t* lengths, int32_t k, int32_t* out_idx,
-                      const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
-                      void* workspace, int64_t workspace_bytes, int32_t pieces, void* hip_stream,
-                      const topk_options* options) {
-    if (batch < 0 || batch > INT32_MAX) return TOPK_ERR_ARG;
+// topk_select_split's checks and launches; with use_scratch, the workspace
+// is the library's scratch array, looked up once every argument has passed.
+int split_select(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols, const int32_t* lengths,
+                 int32_t k, int32_t* out_idx, const int32_t* page_table, int64_t page_table_stride,
+                 int32_t page_size, void* workspace, int64_t workspace_bytes, int32_t pieces, void* hip_stream,
+                 const topk_options* options, bool use_scratch) {
+    if (batch < 0 || batch > (use_scratch ? TOPK_SPLIT_NOALLOC_MAX_BATCH : INT32_MAX)) return TOPK_ERR_ARG;
     if (k < 1 || k > TOPK_MAX_K) return TOPK_ERR_K;
     if (n_cols < 0 || n_cols > INT32_MAX || row_stride < n_cols) return TOPK_ERR_ARG;
     if (pieces < 0 || pieces > kMaxPieces) return TOPK_ERR_ARG;
@@ -820,10 +841,10 @@ int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, in
         if (page_table_stride < (n_cols + page_size - 1) / page_size) return TOPK_ERR_ARG;
     }
     if (batch == 0) return TOPK_OK;
-    if (scores == nullptr || out_idx == nullptr || workspace == nullptr) return TOPK_ERR_ARG;
-    if (workspace_bytes < topk_split_workspace_bytes(batch)) return TOPK_ERR_ARG;
+    if (scores == nullptr || out_idx == nullptr || (!use_scratch && workspace == nullptr)) return TOPK_ERR_ARG;
+    if (!use_scratch && workspace_bytes < split_workspace_bytes(batch)) return TOPK_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(scores) & 15u) != 0) return TOPK_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TOPK_ERR_ALIGN;
+    if (!use_scratch && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TOPK_ERR_ALIGN;
     if (batch > 1 && (row_stride & 3) != 0) return TOPK_ERR_ALIGN;
     // pieces per row: enough workgroups for about four per compute unit, each
     // piece a whole number of load rounds
@@ -842,6 +863,10 @@ int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, in
     const int64_t P = nvec_max > 0 ? (nvec_max + per - 1) / per : 1;
     if (batch * P * kThreads > (int64_t)UINT32_MAX) return TOPK_ERR_ARG;
     if (device_cus() <= 0) return TOPK_ERR_DEVICE;
+    if (use_scratch) {
+        const int st = scratch_address(&workspace);
+        if (st != TOPK_OK) return st;
+    }
 
     char* ws = static_cast<char*>(workspace);
     SplitParams p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride, page_size, k,
@@ -860,6 +885,36 @@ int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, in
                         dim3(kFinThreads), args, 0, st) != hipSuccess)
         return TOPK_ERR_LAUNCH;
     return TOPK_OK;
+}
+
+}  // namespace topk
+
+using namespace topk;
+
+extern "C" {
+
+int64_t topk_split_workspace_bytes(int64_t batch) {
+    if (batch < 0 || batch > INT32_MAX) return -1;
+    return split_workspace_bytes(batch);
+}
+
+int32_t topk_split_capacity(void) { return (int32_t)kSplitCapacity; }
+
+int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                      const int32_t* lengths, int32_t k, int32_t* out_idx,
+                      const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                      void* workspace, int64_t workspace_bytes, int32_t pieces, void* hip_stream,
+                      const topk_options* options) {
+    return split_select(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table, page_table_stride,
+                        page_size, workspace, workspace_bytes, pieces, hip_stream, options, false);
+}
+
+int topk_select_split_noalloc(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                              const int32_t* lengths, int32_t k, int32_t* out_idx, const int32_t* page_table,
+                              int64_t page_table_stride, int32_t page_size, int32_t pieces, void* hip_stream,
+                              const topk_options* options) {
+    return split_select(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table, page_table_stride,
+                        page_size, nullptr, 0, pieces, hip_stream, options, true);
 }
 
 }  // extern "C"

@@ -208,6 +208,33 @@ int topk_select_split(const float* scores, int64_t batch, int64_t row_stride, in
                       void* workspace, int64_t workspace_bytes, int32_t pieces, void* hip_stream,
                       const topk_options* options);
 
+/*
+ * topk_select_split for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same three launches and the same result, with the workspace taken from
+ * a fixed device array inside the library instead of from the caller. The
+ * array holds TOPK_SPLIT_NOALLOC_MAX_BATCH rows (about 16 MiB); each GPU the
+ * library runs this entry on keeps its own copy until the process ends. The
+ * entry allocates and frees nothing; its first call on a device looks the
+ * array's address up once.
+ *
+ * Every call on one GPU shares that GPU's array: calls whose launches can
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * give wrong results; calls ordered on one stream are safe. The array needs
+ * no clearing: each call writes every word it later reads.
+ *
+ * Arguments, results and status codes as for topk_select_split, without
+ * workspace and workspace_bytes; TOPK_ERR_ARG for batch above
+ * TOPK_SPLIT_NOALLOC_MAX_BATCH, TOPK_ERR_DEVICE when no gfx950 device is
+ * current or the array's address cannot be found.
+ */
+#define TOPK_SPLIT_NOALLOC_MAX_BATCH 256
+
+int topk_select_split_noalloc(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols,
+                              const int32_t* lengths, int32_t k, int32_t* out_idx,
+                              const int32_t* page_table, int64_t page_table_stride, int32_t page_size,
+                              int32_t pieces, void* hip_stream, const topk_options* options);
+
 /* Workspace bytes topk_select_split needs for `batch` rows (-1 if batch is
  * negative or above INT32_MAX): a 16-byte header per row, then
  * topk_split_capacity() 8-byte survivor entries per row. */

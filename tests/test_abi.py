@@ -62,8 +62,8 @@ def test_header_declares_the_entry_points():
     assert header_functions() == sorted(
         ["topk_select", "topk_select_ex", "topk_status_string", "topk_max_capacity",
          "topk_short_capacity", "topk_watchdog_trips", "topk_select_split", "topk_split_workspace_bytes",
-         "topk_split_capacity", "topk_select_bf16", "topk_select_bf16_ex", "amax8_varlen",
-         "sort_candidate_blocks"])
+         "topk_split_capacity", "topk_select_split_noalloc", "topk_select_bf16", "topk_select_bf16_ex",
+         "amax8_varlen", "sort_candidate_blocks"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -166,6 +166,16 @@ def test_split_host_argument_checks(lib):
                       pieces=256) == 1
 
 
+def test_noalloc_split_host_argument_checks(lib):
+    lib.topk_select_split_noalloc.argtypes = ARGS[:-1] + [ctypes.c_int32, ctypes.c_void_p,
+                                                           ctypes.POINTER(Options)]
+    na = lambda batch=4, k=16, scores=FAKE, opt=None: lib.topk_select_split_noalloc(
+        scores, batch, 1024, 1024, None, k, FAKE, None, 0, 0, 0, None, ctypes.byref(opt) if opt else None)
+    assert na(batch=257) == 1 and na(batch=-1) == 1  # TOPK_SPLIT_NOALLOC_MAX_BATCH rows at most
+    assert na(batch=0, scores=None) == 0
+    assert na(k=0) == 2 and na(k=2049) == 2
+
+
 def test_split_empty_batch_is_a_no_op(lib):
     assert split_call(lib, batch=0, scores=None, out=None, ws=None, ws_bytes=0) == 0
 
@@ -224,6 +234,9 @@ def test_valid_calls_without_a_device_return_device_error(lib):
     assert call(lib, opt=Options(2, 100, None, 1)) == 4
     assert call(lib, n_cols=40000, row_stride=40000) == 4
     assert split_call(lib) == 4
+    lib.topk_select_split_noalloc.argtypes = ARGS[:-1] + [ctypes.c_int32, ctypes.c_void_p,
+                                                           ctypes.POINTER(Options)]
+    assert lib.topk_select_split_noalloc(FAKE, 4, 1024, 1024, None, 16, FAKE, None, 0, 0, 0, None, None) == 4
     lib.topk_select_bf16.argtypes = ARGS
     assert lib.topk_select_bf16(FAKE, 4, 1024, 1024, None, 16, FAKE, None, 0, 0, None) == 4
     lib.topk_select_bf16_ex.argtypes = ARGS + [ctypes.POINTER(Options)]

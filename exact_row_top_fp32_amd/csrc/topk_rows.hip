@@ -58,6 +58,7 @@ constexpr int kRunLen = 64;                                // floats per contigu
 constexpr int kMaxRuns = 64;                               // runs per sample
 constexpr int kMaxSample = kMaxRuns * kRunLen;             // 4096 keys at most
 constexpr int kFineShift = 14;                             // T to within 2^14 keys (1/512 octave)
+constexpr int kFine = 32 - 2 * kDigitBits;                  // row 0's T: to within 2^10 keys
 constexpr int kSlots = 4;                                  // rows i-1 .. i+2
 constexpr int kTable = 64;                                 // queued rows fetched at a time
 constexpr int kMaxDeferred = 64;                           // full-row rows per workgroup
@@ -122,6 +123,7 @@ struct Shared {
     uint32_t cand_idx[kMaxCand];
     uint32_t heavy[kOrderMaxRows / (kHeavyBucket + 1) + 1];  // queue buckets ranked by scans
     uint32_t nheavy;
+    uint32_t nrank;  // workgroups whose first row is lighter than this one's
     uint32_t ndeferred;
     int32_t deferred[kMaxDeferred];
     int32_t deferred_code[kMaxDeferred];
@@ -219,35 +221,44 @@ __device__ __forceinline__ void defer_row(const Params& p, Shared& sm, SelectLds
 // the queue
 // ----------------------------------------------------------------------------
 
-// Whole workgroup, at start: with no more rows than workgroups, workgroup w
-// takes row w. Otherwise rows with L <= k (dealt round-robin) are written
-// out directly. When every workgroup's share fits one table, the other rows
-// are put in a longest-first order (a counting sort over 2048 length buckets,
-// ties by row index, the same in every workgroup) and this workgroup's share
-// of it is tabled; otherwise rows are dealt in index order, a table at a time.
-__device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
+// The queue is ordered longest first when the batch has at most this many
+// rows and every workgroup's share fits one table; thread t then holds the
+// lengths of rows t, t + kThreads, ... (kLenPer of them), loaded at start.
+__device__ __forceinline__ bool queue_ordered(int64_t batch) {
+    return batch <= kOrderMaxRows && batch <= (int64_t)kTable * gridDim.x;
+}
+constexpr int kLenPer = (kOrderMaxRows + kThreads - 1) / kThreads;
+
+// Whole workgroup, at start. Workgroup w's first row is row w (its length
+// L0), which the kernel starts on before the queue is built; the queue holds
+// the workgroup's other rows. Rows with L <= k (dealt round-robin, row w
+// among them) are written out directly. With no more rows than workgroups
+// there is nothing else. When every workgroup's share fits one table, the
+// rows past the first G are put in a longest-first order (a counting sort
+// over 2048 length buckets, ties by row index, the same in every workgroup),
+// and workgroup w takes positions q, G + q, 2G + q, ... of it, q being the
+// rank of its first row among the first rows, shortest first: the lightest
+// first row goes with the longest row of every round, so the totals even
+// out. Otherwise rows are dealt in index order, a table at a time.
+__device__ __forceinline__ void build_queue(const Params& p, Shared& sm, int64_t L0, const int64_t (&lens)[kLenPer]) {
     using B = BlockScope<kThreads>;
     const int64_t batch = p.batch;
     const uint32_t G = gridDim.x;
     if (batch <= (int64_t)G) {
         // no more rows than workgroups (the grid is min(batch, CUs)):
         // workgroup w takes row w alone, so there is no order to compute
-        const int64_t b = blockIdx.x;
-        const int64_t L = row_len(p, b);
-        if (L <= p.k) direct_row<B>(p, b, L);
+        if (L0 <= p.k) direct_row<B>(p, blockIdx.x, L0);
         if (threadIdx.x == 0) {
             sm.ordered = 1u;
-            sm.nqueue = L > p.k ? 1u : 0u;
-            sm.tab_n = L > p.k ? 1u : 0u;
+            sm.nqueue = 0u;
+            sm.tab_n = 0u;
             sm.tab_pos = 0u;
             sm.tab_round = 0u;
-            sm.tab_b[0] = (int32_t)b;
-            sm.tab_len[0] = (int32_t)L;
         }
         B::sync();
         return;
     }
-    if (batch > kOrderMaxRows || batch > (int64_t)kTable * G) {
+    if (!queue_ordered(batch)) {
         for (int64_t b = blockIdx.x; b < batch; b += G) {
             const int64_t L = row_len(p, b);
             if (L <= p.k) direct_row<B>(p, b, L);
@@ -257,7 +268,7 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
             sm.nqueue = (uint32_t)batch;
             sm.tab_n = (uint32_t)kTable;  // an empty table that asks to be filled
             sm.tab_pos = (uint32_t)kTable;
-            sm.tab_round = 0u;
+            sm.tab_round = 1u;            // from the second row on: row w = snake(0) came first
         }
         B::sync();
         return;
@@ -268,17 +279,20 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
     int32_t* len = reinterpret_cast<int32_t*>(bucket + kOrderMaxRows);
     uint32_t* placed = reinterpret_cast<uint32_t*>(sm.surv[1]);  // rows by bucket, any order within one
     uint32_t* order = placed + kOrderMaxRows;                       // rows by bucket, index order within one
-    uint32_t* direct = sm.skey;    // this workgroup's rows with L <= k
+    uint32_t* direct = sm.skey;    // this workgroup's rows with L <= k (the sample lands after the queue)
     uint32_t* cnt = sm.hist[0];
     uint32_t* start = sm.hist[1];  // rows in higher buckets
     uint32_t* fill = sm.shist;
-    // every length load in flight before the first is used
-    constexpr int kPer = (kOrderMaxRows + kThreads - 1) / kThreads;
-    int64_t lens[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const uint32_t b = threadIdx.x + (uint32_t)j * kThreads;
-        lens[j] = b < n ? row_len(p, b) : 0;
+    constexpr int kPer = kLenPer;
+    static_assert(kThreads >= 256, "the first rows (one per compute unit) sit in every thread's first length");
+    {
+        // this workgroup's rank among the first rows: those with a lighter
+        // load (L if L > k, else 0), ties by workgroup index
+        const int64_t mine = L0 > p.k ? L0 : 0;
+        const int64_t theirs = lens[0] > p.k ? lens[0] : 0;
+        const bool lighter = threadIdx.x < G && (theirs < mine || (theirs == mine && threadIdx.x < blockIdx.x));
+        const uint64_t lm = __ballot(lighter);
+        if (lane_id() == 0 && lm != 0) atomicAdd(&sm.nrank, (uint32_t)__popcll(lm));
     }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -288,8 +302,10 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
         len[b] = (int32_t)L;
         uint32_t d = (uint32_t)kBins;
         if (L > p.k) {
-            d = length_bucket(L, p.n_cols);
-            atomicAdd(&cnt[d], 1u);
+            if (b >= G) {  // the first rows are not queued
+                d = length_bucket(L, p.n_cols);
+                atomicAdd(&cnt[d], 1u);
+            }
         } else if (b % G == blockIdx.x) {
             direct[atomicAdd(&sm.ndirect, 1u)] = b;
         }
@@ -370,7 +386,7 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm) {
     B::sync();
     if (threadIdx.x < 64) {
         const uint32_t j = lane_id();
-        const uint32_t t = snake(j);  // grows with j, so the valid entries lead
+        const uint32_t t = j * G + sm.nrank;  // grows with j, so the valid entries lead
         const bool ok = t < total;
         if (ok) {
             const uint32_t b = order[t];
@@ -415,6 +431,26 @@ __device__ __forceinline__ void fill_table(const Params& p, Shared& sm) {
     WaveScope::sync();
 }
 
+// How a row with L > k is selected: every key kept (L within the capacity),
+// sampled, or the full-row path, as the caller's forced path allows.
+__device__ __forceinline__ uint32_t row_kind(const Params& p, int64_t L) {
+    const int64_t cap = p.capacity;
+    if (p.force_path == TOPK_PATH_FULLROW || (p.force_path == TOPK_PATH_LDS && L > cap)) return kKindFull;
+    if (p.force_path == TOPK_PATH_LDS || (p.force_path == TOPK_PATH_AUTO && L <= cap)) return kKindAll;
+    return kKindSampled;
+}
+
+__device__ __forceinline__ void fill_slot(RowSlot& slot, const Params& p, int64_t b, int64_t L, uint32_t kind) {
+    slot.b = b;
+    slot.L = L;
+    slot.nvec = L >> 2;
+    slot.m = (uint32_t)p.k;
+    slot.T = 0u;                // kKindAll: every key survives
+    slot.sh = 32 - kDigitBits;  // and bins take the top 11 bits
+    slot.kind = kind;
+    slot.valid = 1u;
+}
+
 // One wave: this workgroup's next row into `slot` (invalid once its share is
 // done). Rows with L <= k were written at start; rows forced to the full-row
 // path are deferred on the way. The cutoff of a sampled row is set later.
@@ -434,25 +470,12 @@ __device__ __forceinline__ void claim_row(const Params& p, Shared& sm, RowSlot& 
         if (lane_id() == 0) sm.tab_pos += 1u;
         WaveScope::sync();
         if (L <= p.k) continue;
-        const int64_t cap = p.capacity;
-        uint32_t kind;
-        if (p.force_path == TOPK_PATH_FULLROW || (p.force_path == TOPK_PATH_LDS && L > cap)) kind = kKindFull;
-        else if (p.force_path == TOPK_PATH_LDS || (p.force_path == TOPK_PATH_AUTO && L <= cap)) kind = kKindAll;
-        else kind = kKindSampled;
+        const uint32_t kind = row_kind(p, L);
         if (kind == kKindFull) {
             defer_row(p, sm, own, own_emitted, b, TOPK_ROW_FULL_FORCED);
             continue;
         }
-        if (lane_id() == 0) {
-            slot.b = b;
-            slot.L = L;
-            slot.nvec = L >> 2;
-            slot.m = (uint32_t)p.k;
-            slot.T = 0u;                     // kKindAll: every key survives
-            slot.sh = 32 - kDigitBits;       // and bins take the top 11 bits
-            slot.kind = kind;
-            slot.valid = 1u;
-        }
+        if (lane_id() == 0) fill_slot(slot, p, b, L, kind);
         break;
     }
     WaveScope::sync();
@@ -554,6 +577,40 @@ __device__ __forceinline__ void sample_select(Shared& sm, RowSlot& R, SelectLds 
             }
         }
     };
+    if constexpr (S::kSize > 64) {
+        // The whole workgroup (row 0): 768 lanes hold a few keys each, so
+        // per-lane bounds are weak. The want-th largest key's top 22 bits
+        // come from two fixed 11-bit digit passes instead, the sample's
+        // largest key noted on the first; sm.smax is zero on entry (set at
+        // the kernel's start; the sampler wave sets it itself later).
+        uint32_t smax = 0u;
+        constexpr int kTopShift = 32 - kDigitBits;
+        each_key([&](uint32_t key) {
+            smax = max(smax, key);
+            if (want > 0u) atomicAdd(&lds.hist[key >> kTopShift], 1u);
+        });
+        smax = wave_max(smax);
+        if (lane_id() == 0) atomicMax(&sm.smax, smax);
+        S::sync();
+        uint32_t T = 0u;  // too short to sample, or want out of reach: keep everything
+        if (want > 0u) {
+            const Found f1 = find_rank_bin<S>(lds, want);
+            each_key([&](uint32_t key) {
+                if ((key >> kTopShift) == f1.digit) atomicAdd(&lds.hist[(key >> kFine) & (kBins - 1)], 1u);
+            });
+            S::sync();
+            const Found f2 = find_rank_bin<S>(lds, want - f1.above);
+            T = (f1.digit << kTopShift) | (f2.digit << kFine);
+        }
+        const uint32_t span = sm.smax - T;
+        const int wbits = span == 0u ? 0 : 32 - __clz(span);
+        if (S::rank() == 0) {
+            R.T = T;
+            R.sh = (uint32_t)(wbits > kDigitBits - 1 ? wbits - (kDigitBits - 1) : 0);
+        }
+        S::sync();
+        return;
+    }
     uint32_t top[kQ] = {0u, 0u, 0u, 0u};  // this lane's largest keys, descending
     uint32_t smax = 0u;
     each_key([&](uint32_t key) {
@@ -615,6 +672,35 @@ __device__ __forceinline__ void sample_select(Shared& sm, RowSlot& R, SelectLds 
     }
     S::sync();
 }
+
+// Scope S: a row's sample through registers, for the first row, whose
+// loads are issued while other loads of the same waves are still to come:
+// the compiler then waits for exactly the sample's loads where it stores
+// them to LDS (group t at skey[4t, 4t + 4), as sample_issue places it).
+template <class S>
+struct SampleRegs {
+    static constexpr int kPer = (kMaxSample / 4 + S::kSize - 1) / S::kSize;  // groups per lane
+    f4 v[kPer];
+    __device__ __forceinline__ void issue(const Params& p, int64_t b, int64_t L) {
+        const SamplePlan plan(L);
+        const float* row = p.scores + b * p.row_stride;
+#pragma unroll
+        for (int h = 0; h < kPer; ++h) {
+            const int t = h * S::kSize + (int)S::rank();
+            if (t < plan.nsv) v[h] = *reinterpret_cast<const f4*>(row + plan.group_start(t));
+        }
+    }
+    __device__ __forceinline__ void store(Shared& sm, int64_t L) const {
+        const int nsv = SamplePlan(L).nsv;
+#pragma unroll
+        for (int h = 0; h < kPer; ++h) {
+            const int t = h * S::kSize + (int)S::rank();
+            if (t < nsv)
+                *reinterpret_cast<uint4*>(sm.skey + 4 * t) = make_uint4(
+                    __float_as_uint(v[h].x), __float_as_uint(v[h].y), __float_as_uint(v[h].z), __float_as_uint(v[h].w));
+        }
+    }
+};
 
 template <class S>
 __device__ __forceinline__ void sample_cutoff(const Params& p, Shared& sm, RowSlot& R, SelectLds lds) {
@@ -684,10 +770,11 @@ constexpr uint32_t kEnd = 0xFFFFFFFFu;   // this workgroup's rows are done
 
 // Streaming waves read a row's full groups of 4 scores in chunks of
 // kChunkVec groups; the finisher takes the last L % 4 scores.
-__device__ __forceinline__ uint32_t nchunks(const RowSlot& R) {
-    const int64_t groups = R.L >> 2;
+__device__ __forceinline__ uint32_t nchunks_of(int64_t L) {
+    const int64_t groups = L >> 2;
     return (uint32_t)((groups + kChunkVec - 1) / kChunkVec);
 }
+__device__ __forceinline__ uint32_t nchunks(const RowSlot& R) { return nchunks_of(R.L); }
 
 // A chunk in registers: kUnroll groups of 4 scores per lane.
 struct Chunk {
@@ -1225,6 +1312,8 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         sm.ndeferred = 0u;
         sm.ndirect = 0u;
         sm.nheavy = 0u;
+        sm.nrank = 0u;
+        sm.smax = 0u;
         sm.n_claimed = sm.n_ready = sm.n_finished = 0u;
         sm.last_row = -1;
         sm.abort = 0u;
@@ -1235,34 +1324,95 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         }
     }
     B::sync();
-    build_queue(p, sm);
     const uint32_t cap = (uint32_t)p.capacity;
     const SelectLds sampler_lds{sm.shist, sm.sfound};
 
-    // start: the sampler wave claims rows 0 and 1; the whole workgroup
-    // loads row 0's sample (every wave a share) and finds its cutoff. Each
-    // streaming wave issues its first chunk once the sample is in, so that
-    // the chunk's latency overlaps the cutoff search; issued earlier, the
-    // chunk loads would queue ahead of the sample's.
+    // start. Workgroup w's first row is row w in every queue layout, so it
+    // is known before the queue is built: its sample's loads go out before
+    // the length sort, whose time they overlap. Once the queue is built, the
+    // sampler wave claims the next row, each streaming wave issues a chunk of
+    // row 0 (issued earlier, the chunks' loads, 80 KB per compute unit,
+    // delay the sample's and slow the sort), the whole workgroup finds row
+    // 0's cutoff from the sample while they are in flight, and the roles
+    // start.
+    const int64_t b0 = blockIdx.x;  // the grid is min(batch, CUs)
+    // every length load in flight before the first is used
+    const bool ordered = p.batch > (int64_t)gridDim.x && queue_ordered(p.batch);
+    int64_t L0 = p.n_cols;
+    int64_t lens[kLenPer];
+#pragma unroll
+    for (int j = 0; j < kLenPer; ++j) lens[j] = p.n_cols;
+    if (p.lengths != nullptr) {  // unconditional loads (clamped rows), so that one wait covers all
+        L0 = p.lengths[b0];
+#pragma unroll
+        for (int j = 0; j < kLenPer; ++j) {
+            const int64_t b = threadIdx.x + (int64_t)j * kThreads;
+            lens[j] = p.lengths[b < p.batch ? b : p.batch - 1];
+        }
+    }
+    L0 = L0 < 0 ? 0 : (L0 > p.n_cols ? p.n_cols : L0);
+#pragma unroll
+    for (int j = 0; j < kLenPer; ++j) {
+        const int64_t b = threadIdx.x + (int64_t)j * kThreads;
+        const int64_t L = lens[j] < 0 ? 0 : (lens[j] > p.n_cols ? p.n_cols : lens[j]);
+        lens[j] = ordered && b < p.batch ? L : 0;
+    }
+    const uint32_t kind0 = L0 > p.k ? row_kind(p, L0) : kKindFull;
+    const bool stream0 = L0 > p.k && kind0 != kKindFull;  // row 0 is this workgroup's first streamed row
+    // Its loads go out before the queue is built when that needs no more
+    // length loads: one row per workgroup, or the ordered queue.
+    const bool early = stream0 && (ordered || p.batch <= (int64_t)gridDim.x);
+    const bool sampled0 = early && kind0 == kKindSampled;
+    SampleRegs<B> sample;
+    if (sampled0) sample.issue(p, b0, L0);
+    Chunk a, b;
+    Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0};
+    if (stream0 && threadIdx.x == 0) {
+        fill_slot(sm.slot[0], p, b0, L0, kind0);
+        sm.chunk_next[0] = early ? (uint32_t)kStreamers : 0u;
+    }
+    build_queue(p, sm, L0, lens);
     if (wave_id() == 1) {
-        claim_row(p, sm, sm.slot[0], sampler_lds, &sm.semitted);
+        if (L0 > p.k && kind0 == kKindFull) defer_row(p, sm, sampler_lds, &sm.semitted, b0, TOPK_ROW_FULL_FORCED);
+        if (!stream0) claim_row(p, sm, sm.slot[0], sampler_lds, &sm.semitted);
         claim_row(p, sm, sm.slot[1], sampler_lds, &sm.semitted);
         if (lane_id() == 0) sm.n_claimed = 2u;
     }
+    if (sampled0) sample.store(sm, L0);
     B::sync();
-    const bool sampled0 = sm.slot[0].valid && sm.slot[0].kind == kKindSampled;
-    if (sampled0) sample_load<B>(p, sm, sm.slot[0]);
-    Chunk a, b;
-    Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0};
-    if (wave_id() >= kFirstStreamer) {
-        // rows 0-1 only: later rows are not claimed before the roles start
-        st.c = st.grab(st.i, 1, false);
-        st.load(a, st.i, st.c);
+    // Row 0 when it comes after the queue (row w of a batch dealt in index
+    // order, or the queue's first row when row w was written directly or
+    // deferred): its sample, then its chunks.
+    const bool late = !early && sm.slot[0].valid;
+    const bool late_sampled = late && sm.slot[0].kind == kKindSampled;
+    if (late_sampled) sample_load<B>(p, sm, sm.slot[0]);
+    {
+        // Each streaming wave's first chunk, from one load site (its
+        // registers then stay where the roles use them, and nothing waits
+        // for them before the roles start). Row 0 from the start: streaming
+        // wave s takes chunk s, a wave left without one is done with row 0.
+        // After the queue: the next chunk of rows 0-1 (later rows are not
+        // claimed yet). Waves without a chunk issue loads that touch no
+        // memory.
+        const bool streamer = wave_id() >= kFirstStreamer;
+        uint32_t c = kNone;
+        if (streamer && early) {
+            const uint32_t c0 = wave_id() - kFirstStreamer;
+            if (c0 < nchunks_of(L0)) {
+                c = c0;
+            } else {
+                st.leave(0);
+                st.i = 1;
+            }
+        } else if (streamer && late) {
+            c = st.grab(st.i, 1, false);
+        }
+        const RowSlot& R = sm.slot[(c < kNone ? st.i : 0) % kSlots];
+        load_chunk(a, c < kNone ? p.scores + R.b * p.row_stride : p.scores, c < kNone ? R.L : 0, c);
+        st.c = c;
     }
-    if (sampled0) {
-        B::sync();
-        sample_select<B>(sm, sm.slot[0], sampler_lds);
-    }
+    if (late_sampled) B::sync();
+    if (sampled0 || late_sampled) sample_select<B>(sm, sm.slot[0], sampler_lds);
     if (threadIdx.x == 0) sm.n_ready = 1u;
     B::sync();
 

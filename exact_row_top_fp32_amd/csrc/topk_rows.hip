@@ -1266,13 +1266,15 @@ __device__ __forceinline__ void finish_sampled_wg(const Params& p, Shared& sm, c
 }
 
 // Scope S: finishes row R from buffer x, or defers it to the full-row path
-// when its survivors overflowed the buffer or fell short of m. Leaves buffer
-// x's counters and histogram zero.
+// when its survivors overflowed the buffer or fell short of m (returns
+// whether it did, the same in every lane). One wave (rows before the last)
+// leaves buffer x's counters and histogram zero.
 template <class S>
-__device__ __forceinline__ void finish_row(const Params& p, Shared& sm, const RowSlot& R, int x, uint32_t cap) {
+__device__ __forceinline__ bool finish_row(const Params& p, Shared& sm, const RowSlot& R, int x, uint32_t cap) {
     const uint32_t n = sm.count[x];
     const SelectLds lds{sm.hist[x], sm.found};
-    if (n > cap || n < R.m) {
+    const bool deferred = n > cap || n < R.m;
+    if (deferred) {
         const int code = n > cap ? TOPK_ROW_FULL_OVERFLOW : TOPK_ROW_FULL_UNDERFLOW;
         if (S::first_wave()) defer_row(p, sm, lds, &sm.emitted, R.b, code);
     } else {
@@ -1285,14 +1287,21 @@ __device__ __forceinline__ void finish_row(const Params& p, Shared& sm, const Ro
         }
         if (S::rank() == 0) put_stats(p, R.b, R.kind == kKindAll ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED, n);
     }
-    S::sync();
-    if (S::rank() == 0) {
-        sm.count[x] = 0u;
-        sm.vmax[x] = 0u;
-        sm.emitted = 0u;
-        sm.ncand = 0u;
+    if constexpr (S::kSize == 64) {
+        S::sync();
+        if (S::rank() == 0) {
+            sm.count[x] = 0u;
+            sm.vmax[x] = 0u;
+            sm.emitted = 0u;
+            sm.ncand = 0u;
+        }
+        S::sync();
     }
-    S::sync();
+    // the whole workgroup finishes only a workgroup's last row: no row
+    // uses the buffer after it, and the full-row passes that may follow
+    // reset their own counter, so nothing is cleared (a barrier precedes
+    // them)
+    return deferred;
 }
 
 // ----------------------------------------------------------------------------
@@ -1466,10 +1475,12 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     }
     B::sync();
     if (sm.abort != 0u && threadIdx.x == 0) atomicAdd(&g_watchdog_trips, 1u);
+    bool full_rows = sm.ndeferred != 0u;  // rows deferred while the roles ran
     if (sm.last_row >= 0 && sm.abort == 0u) {
         const int r = sm.last_row;
-        finish_row<B>(p, sm, sm.slot[r % kSlots], r & 1, cap);
+        full_rows |= finish_row<B>(p, sm, sm.slot[r % kSlots], r & 1, cap);
     }
+    if (!full_rows) return;
     B::sync();
     const uint32_t nd = sm.ndeferred < (uint32_t)kMaxDeferred ? sm.ndeferred : (uint32_t)kMaxDeferred;
     for (uint32_t j = 0; j < nd; ++j)

@@ -119,8 +119,9 @@ struct Shared {
     uint32_t ncand;
     uint32_t smax;
     uint32_t slo;
-    uint32_t cand_key[kMaxCand];
-    uint32_t cand_idx[kMaxCand];
+    alignas(16) uint32_t cand_key[kMaxCand];
+    alignas(16) uint32_t cand_idx[kMaxCand];
+    uint32_t take_cand;  // the last row's slots: taken (low 16 bits) and candidates (high 16)
     uint32_t heavy[kOrderMaxRows / (kHeavyBucket + 1) + 1];  // queue buckets ranked by scans
     uint32_t nheavy;
     uint32_t nrank;  // workgroups whose first row is lighter than this one's
@@ -997,15 +998,23 @@ struct Streamer {
 // finishing a row from its survivors
 // ----------------------------------------------------------------------------
 
-// One wave: lane l < nc holds candidate (key kj, index ij); returns how many
-// of the nc candidates rank before it (key descending, index ascending).
-// Candidates are read from the other lanes' registers, not from LDS.
-__device__ __forceinline__ uint32_t rank_in_wave(uint32_t kj, uint32_t ij, uint32_t nc) {
+// One wave: lane l < nc holds candidate (key kj, index ij), and all nc
+// candidates are also in LDS (keys, idxs: 16-byte aligned, room for
+// kMaxCand); returns how many of them rank before it (key descending, index
+// ascending). Every lane reads the candidates with broadcast LDS loads, four
+// at a time, all independent of each other (entries past nc are read but not
+// counted): a cross-lane read per candidate would cost a dependent
+// register-to-scalar round trip each.
+__device__ __forceinline__ uint32_t rank_in_wave(const uint32_t* keys, const uint32_t* idxs, uint32_t kj,
+                                                 uint32_t ij, uint32_t nc) {
     uint32_t r = 0;
-    for (uint32_t i = 0; i < nc; ++i) {
-        const uint32_t ki = __builtin_amdgcn_readlane(kj, i);
-        const uint32_t ii = __builtin_amdgcn_readlane(ij, i);
-        r += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
+    for (uint32_t i = 0; i < nc; i += 4) {
+        const uint4 k4 = *reinterpret_cast<const uint4*>(keys + i);
+        const uint4 i4 = *reinterpret_cast<const uint4*>(idxs + i);
+        r += (k4.x > kj || (k4.x == kj && i4.x < ij)) ? 1u : 0u;
+        r += (i + 1 < nc && (k4.y > kj || (k4.y == kj && i4.y < ij))) ? 1u : 0u;
+        r += (i + 2 < nc && (k4.z > kj || (k4.z == kj && i4.z < ij))) ? 1u : 0u;
+        r += (i + 3 < nc && (k4.w > kj || (k4.w == kj && i4.w < ij))) ? 1u : 0u;
     }
     return r;
 }
@@ -1142,7 +1151,7 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
             const bool have = lane < nc;
             const uint32_t kj = have ? sm.cand_key[lane] : 0u;
             const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
-            const uint32_t r = rank_in_wave(kj, ij, nc);
+            const uint32_t r = rank_in_wave(sm.cand_key, sm.cand_idx, kj, ij, nc);
             if (have && r < need) stage[next + r] = ij;
         }
         S::sync();
@@ -1168,7 +1177,7 @@ __device__ __forceinline__ void finish_sampled(const Params& p, Shared& sm, cons
             const bool have = lane < nc;
             const uint32_t kj = have ? sm.cand_key[lane] : 0u;
             const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
-            const uint32_t r = rank_in_wave(kj, ij, nc);
+            const uint32_t r = rank_in_wave(sm.cand_key, sm.cand_idx, kj, ij, nc);
             out.append(have && r < need, ij);
         }
     }
@@ -1235,8 +1244,13 @@ __device__ __forceinline__ void finish_sampled_wg(const Params& p, Shared& sm, c
         tmask |= (uint32_t)(ok & !take_none & (kv >= t_take)) << j;
         cmask |= (uint32_t)(ok & !whole & (kv - t_lo <= c_span)) << j;
     }
-    uint32_t ts = wave_reserve_count(&sm.emitted, (uint32_t)__popc(tmask));
-    uint32_t cs = wave_reserve_count(&sm.ncand, (uint32_t)__popc(cmask));
+    // both reservations in one: taken entries in the low 16 bits, candidates
+    // in the high 16 (at most m <= 2048 and the buffer's capacity, so the
+    // low half never carries)
+    const uint32_t slots =
+        wave_reserve_count(&sm.take_cand, (uint32_t)__popc(tmask) | ((uint32_t)__popc(cmask) << 16));
+    uint32_t ts = slots & 0xFFFFu;
+    uint32_t cs = slots >> 16;
     const OutRow out = out_row(p, R.b, m, nullptr);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -1260,7 +1274,7 @@ __device__ __forceinline__ void finish_sampled_wg(const Params& p, Shared& sm, c
         const bool have = lane < nc;
         const uint32_t kj = have ? sm.cand_key[lane] : 0u;
         const uint32_t ij = have ? sm.cand_idx[lane] : 0u;
-        const uint32_t r = rank_in_wave(kj, ij, nc);
+        const uint32_t r = rank_in_wave(sm.cand_key, sm.cand_idx, kj, ij, nc);
         if (have && r < need) out.row[m - need + r] = out.map(ij);
     }
 }
@@ -1323,6 +1337,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         sm.nheavy = 0u;
         sm.nrank = 0u;
         sm.smax = 0u;
+        sm.take_cand = 0u;
         sm.n_claimed = sm.n_ready = sm.n_finished = 0u;
         sm.last_row = -1;
         sm.abort = 0u;

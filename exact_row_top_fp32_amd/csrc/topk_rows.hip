@@ -58,12 +58,10 @@ constexpr int kRunLen = 64;                                // floats per contigu
 constexpr int kMaxRuns = 64;                               // runs per sample
 constexpr int kMaxSample = kMaxRuns * kRunLen;             // 4096 keys at most
 constexpr int kFineShift = 14;                             // T to within 2^14 keys (1/512 octave)
-constexpr int kFine = 32 - 2 * kDigitBits;                  // row 0's T: to within 2^10 keys
 constexpr int kSlots = 4;                                  // rows i-1 .. i+2
 constexpr int kTable = 64;                                 // queued rows fetched at a time
 constexpr int kMaxDeferred = 64;                           // full-row rows per workgroup
 constexpr int kOrderMaxRows = 2048;                        // longest-first order up to this batch
-constexpr int kHeavyBucket = 64;                           // larger length buckets: ranked by a scan
 
 constexpr uint32_t kKindSampled = 0, kKindAll = 1, kKindFull = 2;
 constexpr uint64_t kWatchdogTicks = 10ull * 100000000ull;  // 10 s
@@ -122,14 +120,12 @@ struct Shared {
     alignas(16) uint32_t cand_key[kMaxCand];
     alignas(16) uint32_t cand_idx[kMaxCand];
     uint32_t take_cand;  // the last row's slots: taken (low 16 bits) and candidates (high 16)
-    uint32_t heavy[kOrderMaxRows / (kHeavyBucket + 1) + 1];  // queue buckets ranked by scans
-    uint32_t nheavy;
-    uint32_t nrank;  // workgroups whose first row is lighter than this one's
     uint32_t ndeferred;
     int32_t deferred[kMaxDeferred];
     int32_t deferred_code[kMaxDeferred];
     int32_t tab_b[kTable];
     int32_t tab_len[kTable];
+    uint32_t nrank;  // workgroups whose first row is lighter than this one's
     uint32_t ndirect;
     uint32_t tab_n;
     uint32_t tab_pos;
@@ -230,18 +226,164 @@ __device__ __forceinline__ bool queue_ordered(int64_t batch) {
 }
 constexpr int kLenPer = (kOrderMaxRows + kThreads - 1) / kThreads;
 
-// Whole workgroup, at start. Workgroup w's first row is row w (its length
-// L0), which the kernel starts on before the queue is built; the queue holds
-// the workgroup's other rows. Rows with L <= k (dealt round-robin, row w
-// among them) are written out directly. With no more rows than workgroups
-// there is nothing else. When every workgroup's share fits one table, the
-// rows past the first G are put in a longest-first order (a counting sort
-// over 2048 length buckets, ties by row index, the same in every workgroup),
-// and workgroup w takes positions q, G + q, 2G + q, ... of it, q being the
-// rank of its first row among the first rows, shortest first: the lightest
-// first row goes with the longest row of every round, so the totals even
-// out. Otherwise rows are dealt in index order, a table at a time.
-__device__ __forceinline__ void build_queue(const Params& p, Shared& sm, int64_t L0, const int64_t (&lens)[kLenPer]) {
+// Where in LDS the ordered queue is made: survivor buffer 1 and its
+// histogram, both free until row 1 is claimed, so that the sampler wave can
+// make the table while row 0 streams into buffer 0.
+struct QueueLds {
+    uint32_t* bucket;  // per row: its length bucket; kBins for L <= k or a first row
+    int32_t* len;      // per row: its clamped length
+    uint32_t* direct;  // this workgroup's rows with L <= k (at most kTable)
+    uint32_t* cnt;     // per length bucket: queued rows in it (zero on entry and on exit)
+};
+static_assert(2 * kCapacity >= 2 * kOrderMaxRows + kTable, "the queue fits one survivor buffer");
+
+__device__ __forceinline__ QueueLds queue_lds(Shared& sm) {
+    uint32_t* b1 = reinterpret_cast<uint32_t*>(sm.surv[1]);
+    return QueueLds{b1, reinterpret_cast<int32_t*>(b1 + kOrderMaxRows), b1 + 2 * kOrderMaxRows, sm.hist[1]};
+}
+
+// The ordered queue: the rows past the first G, longest first (by 2048
+// length buckets, ties by row index, the same order in every workgroup);
+// workgroup w takes positions q, G + q, 2G + q, ... of it, q being the rank
+// of its first row among the first rows, shortest first: the lightest first
+// row goes with the longest row of every round, so the totals even out.
+// Rows with L <= k (dealt round-robin, row w among them) are written out
+// directly.
+//
+// Two parts. The count, by the whole workgroup from the lengths its threads
+// loaded at start: each row's length and bucket, the bucket counts, the
+// direct rows and q.
+__device__ __forceinline__ void queue_count(const Params& p, Shared& sm, const QueueLds& q, int64_t L0,
+                                            const int64_t (&lens)[kLenPer]) {
+    const uint32_t n = (uint32_t)p.batch;
+    const uint32_t G = gridDim.x;
+    static_assert(kThreads >= 256, "the first rows (one per compute unit) sit in every thread's first length");
+    {
+        // this workgroup's rank among the first rows: those with a lighter
+        // load (L if L > k, else 0), ties by workgroup index
+        const int64_t mine = L0 > p.k ? L0 : 0;
+        const int64_t theirs = lens[0] > p.k ? lens[0] : 0;
+        const bool lighter = threadIdx.x < G && (theirs < mine || (theirs == mine && threadIdx.x < blockIdx.x));
+        const uint64_t lm = __ballot(lighter);
+        if (lane_id() == 0 && lm != 0) atomicAdd(&sm.nrank, (uint32_t)__popcll(lm));
+    }
+#pragma unroll
+    for (int j = 0; j < kLenPer; ++j) {
+        const uint32_t b = threadIdx.x + (uint32_t)j * kThreads;
+        if (b >= n) break;
+        const int64_t L = lens[j];
+        q.len[b] = (int32_t)L;
+        uint32_t d = (uint32_t)kBins;
+        if (L > p.k) {
+            if (b >= G) {  // the first rows are not queued
+                d = length_bucket(L, p.n_cols);
+                atomicAdd(&q.cnt[d], 1u);
+            }
+        } else if (b % G == blockIdx.x) {
+            q.direct[atomicAdd(&sm.ndirect, 1u)] = b;
+        }
+        q.bucket[b] = d;
+    }
+}
+
+// The table, by one wave from the count in LDS (no memory loads: while rows
+// stream, a load waits behind the streaming waves' loads). No sort: each
+// position t is found by rank, its bucket from running sums of the bucket
+// counts (higher buckets first), then its row as the one of rank
+// t - (rows in higher buckets) among the bucket's rows, by index, from a
+// running count over the rows. `first(b, L)` is called on the first
+// position's row as soon as it is known. Then the direct rows. Leaves the
+// counts zero.
+template <class First>
+__device__ __forceinline__ void queue_table(const Params& p, Shared& sm, const QueueLds& q, First&& first) {
+    static_assert(kBins == 64 * 32, "32 buckets per lane");
+    const uint32_t lane = lane_id();
+    const uint32_t n = (uint32_t)p.batch;
+    const uint32_t G = gridDim.x;
+    const uint32_t ns = (n + 63u) / 64u;  // rows in strides of 64
+    // lane l sums buckets 32l .. 32l + 31; higher buckets come first
+    uint32_t own = 0;
+    {
+        const uint4* c4 = reinterpret_cast<const uint4*>(q.cnt + 32 * lane);
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = c4[j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) own += v[j].x + v[j].y + v[j].z + v[j].w;
+    }
+    const uint32_t incl = wave_inclusive_sum(own);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    const uint32_t above = total - incl;  // queued rows in higher lanes' buckets
+    const uint32_t q0 = sm.nrank;
+    uint32_t nt = 0;
+    for (uint32_t e = 0; e < (uint32_t)kTable; ++e) {
+        const uint32_t t = e * G + q0;
+        if (t >= total) break;
+        // the lane whose buckets hold position t, then the bucket: lanes
+        // j < 32 take that lane's buckets, the highest first
+        const int ol = __ffsll((unsigned long long)__ballot(above <= t && t < above + own)) - 1;
+        const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)above, ol);
+        const uint32_t cj = lane < 32u ? q.cnt[32u * (uint32_t)ol + 31u - lane] : 0u;
+        const uint32_t ci = wave_inclusive_sum(cj);
+        const int jl = __ffsll((unsigned long long)__ballot(lane < 32u && base + ci - cj <= t && t < base + ci)) - 1;
+        const uint32_t d = 32u * (uint32_t)ol + 31u - (uint32_t)jl;
+        uint32_t r = t - base - (uint32_t)__builtin_amdgcn_readlane((int)(ci - cj), jl);
+        // the row of rank r among the bucket's rows, by index: 64 rows at a
+        // time, four strides' reads issued together
+        uint32_t row = 0;
+        bool found = false;
+        for (uint32_t j0 = 0; j0 < ns && !found; j0 += 4u) {
+            uint32_t bv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t b = (j0 + (uint32_t)u) * 64u + lane;
+                bv[u] = b < n ? q.bucket[b] : (uint32_t)kBins;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint64_t m = __ballot(bv[u] == d);
+                const uint32_t pc = (uint32_t)__popcll(m);
+                if (!found && r < pc) {
+                    const int rl = __ffsll((unsigned long long)__ballot(bv[u] == d && lanes_below(m) == r)) - 1;
+                    row = (j0 + (uint32_t)u) * 64u + (uint32_t)rl;
+                    found = true;
+                } else if (!found) {
+                    r -= pc;
+                }
+            }
+        }
+        const int32_t len = __builtin_amdgcn_readfirstlane(q.len[row]);
+        if (lane == 0) {
+            sm.tab_b[e] = (int32_t)row;
+            sm.tab_len[e] = len;
+        }
+        if (e == 0) first((int64_t)row, (int64_t)len);
+        nt = e + 1u;
+    }
+    uint4* z4 = reinterpret_cast<uint4*>(q.cnt + 32 * lane);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z4[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (lane == 0) {
+        sm.ordered = 1u;
+        sm.nqueue = total;
+        sm.tab_n = nt;
+        sm.tab_pos = 0u;
+        sm.tab_round = 0u;
+    }
+    WaveScope::sync();
+    const uint32_t nd = sm.ndirect;
+    for (uint32_t j = 0; j < nd; ++j) {
+        const uint32_t b = q.direct[j];
+        direct_row<WaveScope>(p, b, q.len[b]);
+    }
+    WaveScope::sync();
+}
+
+// Whole workgroup, at start, for a queue that is not ordered: with no more
+// rows than workgroups there is nothing to queue (workgroup w takes row w);
+// larger batches than one table per workgroup holds are dealt in index
+// order, a table at a time.
+__device__ __forceinline__ void build_queue(const Params& p, Shared& sm, int64_t L0) {
     using B = BlockScope<kThreads>;
     const int64_t batch = p.batch;
     const uint32_t G = gridDim.x;
@@ -259,156 +401,16 @@ __device__ __forceinline__ void build_queue(const Params& p, Shared& sm, int64_t
         B::sync();
         return;
     }
-    if (!queue_ordered(batch)) {
-        for (int64_t b = blockIdx.x; b < batch; b += G) {
-            const int64_t L = row_len(p, b);
-            if (L <= p.k) direct_row<B>(p, b, L);
-        }
-        if (threadIdx.x == 0) {
-            sm.ordered = 0u;
-            sm.nqueue = (uint32_t)batch;
-            sm.tab_n = (uint32_t)kTable;  // an empty table that asks to be filled
-            sm.tab_pos = (uint32_t)kTable;
-            sm.tab_round = 1u;            // from the second row on: row w = snake(0) came first
-        }
-        B::sync();
-        return;
+    for (int64_t b = blockIdx.x; b < batch; b += G) {
+        const int64_t L = row_len(p, b);
+        if (L <= p.k) direct_row<B>(p, b, L);
     }
-    const uint32_t n = (uint32_t)batch;
-    static_assert(2 * kCapacity >= 2 * kOrderMaxRows, "the queue fits the survivor buffers");
-    uint32_t* bucket = reinterpret_cast<uint32_t*>(sm.surv[0]);  // per row: its length bucket, kBins for L <= k
-    int32_t* len = reinterpret_cast<int32_t*>(bucket + kOrderMaxRows);
-    uint32_t* placed = reinterpret_cast<uint32_t*>(sm.surv[1]);  // rows by bucket, any order within one
-    uint32_t* order = placed + kOrderMaxRows;                       // rows by bucket, index order within one
-    uint32_t* direct = sm.skey;    // this workgroup's rows with L <= k (the sample lands after the queue)
-    uint32_t* cnt = sm.hist[0];
-    uint32_t* start = sm.hist[1];  // rows in higher buckets
-    uint32_t* fill = sm.shist;
-    constexpr int kPer = kLenPer;
-    static_assert(kThreads >= 256, "the first rows (one per compute unit) sit in every thread's first length");
-    {
-        // this workgroup's rank among the first rows: those with a lighter
-        // load (L if L > k, else 0), ties by workgroup index
-        const int64_t mine = L0 > p.k ? L0 : 0;
-        const int64_t theirs = lens[0] > p.k ? lens[0] : 0;
-        const bool lighter = threadIdx.x < G && (theirs < mine || (theirs == mine && threadIdx.x < blockIdx.x));
-        const uint64_t lm = __ballot(lighter);
-        if (lane_id() == 0 && lm != 0) atomicAdd(&sm.nrank, (uint32_t)__popcll(lm));
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const uint32_t b = threadIdx.x + (uint32_t)j * kThreads;
-        if (b >= n) break;
-        const int64_t L = lens[j];
-        len[b] = (int32_t)L;
-        uint32_t d = (uint32_t)kBins;
-        if (L > p.k) {
-            if (b >= G) {  // the first rows are not queued
-                d = length_bucket(L, p.n_cols);
-                atomicAdd(&cnt[d], 1u);
-            }
-        } else if (b % G == blockIdx.x) {
-            direct[atomicAdd(&sm.ndirect, 1u)] = b;
-        }
-        bucket[b] = d;
-    }
-    B::sync();
-    if (threadIdx.x < 64) {  // suffix sums of the bucket counts, 32 buckets per lane
-        // the lane's counts in registers (8 16-byte LDS reads issued together),
-        // its starts written back the same way: interleaved single reads and
-        // writes of LDS would each wait for the one before
-        const uint32_t lane = lane_id();
-        const uint4* c4 = reinterpret_cast<const uint4*>(cnt + 32 * lane);
-        uint32_t c[32];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint4 v = c4[q];
-            c[4 * q + 0] = v.x;
-            c[4 * q + 1] = v.y;
-            c[4 * q + 2] = v.z;
-            c[4 * q + 3] = v.w;
-        }
-        uint32_t own = 0;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) own += c[j];
-        const uint32_t incl = wave_inclusive_sum(own);
-        const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
-        uint32_t above = total - incl;  // rows in the buckets of higher lanes
-        uint32_t sv[32];
-#pragma unroll
-        for (int j = 31; j >= 0; --j) {
-            sv[j] = above;
-            above += c[j];
-        }
-        uint4* s4 = reinterpret_cast<uint4*>(start + 32 * lane);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) s4[q] = make_uint4(sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]);
-#pragma unroll
-        for (int j = 0; j < 32; ++j)
-            if (c[j] > (uint32_t)kHeavyBucket) sm.heavy[atomicAdd(&sm.nheavy, 1u)] = 32 * lane + j;
-        if (lane == 0) sm.nqueue = total;
-    }
-    B::sync();
-    for (uint32_t b = threadIdx.x; b < n; b += kThreads) {
-        const uint32_t d = bucket[b];
-        if (d < (uint32_t)kBins) placed[start[d] + atomicAdd(&fill[d], 1u)] = b;
-    }
-    B::sync();
-    const uint32_t total = sm.nqueue;
-    for (uint32_t t = threadIdx.x; t < total; t += kThreads) {
-        const uint32_t b = placed[t];
-        const uint32_t d = bucket[b];
-        const uint32_t s0 = start[d], s1 = s0 + cnt[d];
-        if (s1 - s0 > (uint32_t)kHeavyBucket) continue;
-        uint32_t r = 0;
-        for (uint32_t u = s0; u < s1; ++u) r += placed[u] < b ? 1u : 0u;
-        order[s0 + r] = b;
-    }
-    // a bucket of many rows (rows of one length, say): ranks by index from
-    // a workgroup-wide scan of "row b is in the bucket" over b
-    const uint32_t nh = sm.nheavy;
-    for (uint32_t h = 0; h < nh; ++h) {
-        const uint32_t d = sm.heavy[h];
-        const uint32_t b0 = threadIdx.x * (uint32_t)kPer;
-        uint32_t own = 0;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) own += b0 + j < n && bucket[b0 + j] == d ? 1u : 0u;
-        const uint32_t incl = wave_inclusive_sum(own);
-        uint32_t* wave_total = fill;  // free once the rows are placed
-        B::sync();
-        if (lane_id() == 63) wave_total[wave_id()] = incl;
-        B::sync();
-        uint32_t r = start[d] + incl - own;
-        for (uint32_t w = 0; w < wave_id(); ++w) r += wave_total[w];
-#pragma unroll
-        for (int j = 0; j < kPer; ++j)
-            if (b0 + j < n && bucket[b0 + j] == d) order[r++] = b0 + j;
-    }
-    B::sync();
-    if (threadIdx.x < 64) {
-        const uint32_t j = lane_id();
-        const uint32_t t = j * G + sm.nrank;  // grows with j, so the valid entries lead
-        const bool ok = t < total;
-        if (ok) {
-            const uint32_t b = order[t];
-            sm.tab_b[j] = (int32_t)b;
-            sm.tab_len[j] = len[b];
-        }
-        const uint32_t nt = (uint32_t)__popcll(__ballot(ok));
-        if (j == 0) {
-            sm.ordered = 1u;
-            sm.tab_n = nt;
-            sm.tab_pos = 0u;
-            sm.tab_round = 0u;
-        }
-    }
-    const uint32_t nd = sm.ndirect;
-    B::sync();
-    for (int i = threadIdx.x; i < kBins; i += kThreads) cnt[i] = start[i] = fill[i] = 0u;
-    if (threadIdx.x == 0) sm.nheavy = 0u;
-    for (uint32_t j = 0; j < nd; ++j) {
-        const uint32_t b = direct[j];
-        direct_row<B>(p, b, len[b]);
+    if (threadIdx.x == 0) {
+        sm.ordered = 0u;
+        sm.nqueue = (uint32_t)batch;
+        sm.tab_n = (uint32_t)kTable;  // an empty table that asks to be filled
+        sm.tab_pos = (uint32_t)kTable;
+        sm.tab_round = 1u;            // from the second row on: row w = snake(0) came first
     }
     B::sync();
 }
@@ -482,20 +484,23 @@ __device__ __forceinline__ void claim_row(const Params& p, Shared& sm, RowSlot& 
     WaveScope::sync();
 }
 
-// sample_cutoff, scope S: the cutoff of a sampled row. A sample of `runs` runs of 64
-// contiguous scores spread evenly over [0, L) gives T at or just below the
-// want-th largest sample key, want set so that the expected survivor count
-// sits several standard deviations above m (the number of sample keys above
-// the true m-th key is binomial).
+// The cutoff of a sampled row. A sample of `runs` runs of 64 contiguous
+// scores spread evenly over [0, L) gives T at or just below the want-th
+// largest sample key, want set so that the expected survivor count sits
+// several standard deviations above m (the number of sample keys above the
+// true m-th key is binomial).
 //
 // The sample goes straight from HBM to LDS (every load in flight at once, no
-// registers held). Each lane then keeps its q = ceil(want / lanes) largest
-// keys; the smallest of the lanes' q-th largest, lo, has at least want keys
-// at or above it (lo = 0 when q is too large to keep). A histogram of the
-// keys in [lo, sample max], in 2048 bins, locates the want-th largest; its
-// bin is narrowed by further histograms until bins are at most 2^kFineShift
-// keys wide, and T is the lower edge of the last bin. The bin width of the
+// registers held), except row 0's, which goes through registers. With one
+// wave, each lane then keeps its q = ceil(want / lanes) largest keys; the
+// smallest of the lanes' q-th largest, lo, has at least want keys at or
+// above it (lo = 0 when q is too large to keep). The whole workgroup takes
+// a bound per wave instead (see sample_select). A histogram of the keys in
+// [lo, sample max], in 2048 bins, locates the want-th largest; its bin is
+// narrowed by further histograms until bins are at most 2^kFineShift keys
+// wide, and T is the lower edge of the last bin. The bin width of the
 // survivor histogram makes [T, sample max] cover about half its bins.
+//
 // Where a row's sample lies: `runs` runs of kRunLen scores; run r starts at
 // floor(r (L - 64) / (runs - 1)) rounded down to a multiple of 4.
 struct SamplePlan {
@@ -553,7 +558,7 @@ __device__ __forceinline__ void sample_load(const Params& p, Shared& sm, const R
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
-// Scope S: the cutoff of row R from the sample in LDS (see sample_cutoff).
+// Scope S: the cutoff of row R from the sample in LDS.
 template <class S>
 __device__ __forceinline__ void sample_select(Shared& sm, RowSlot& R, SelectLds lds) {
     constexpr int kPer = (kMaxSample / 4 + S::kSize - 1) / S::kSize;  // groups per lane
@@ -579,31 +584,85 @@ __device__ __forceinline__ void sample_select(Shared& sm, RowSlot& R, SelectLds 
         }
     };
     if constexpr (S::kSize > 64) {
-        // The whole workgroup (row 0): 768 lanes hold a few keys each, so
-        // per-lane bounds are weak. The want-th largest key's top 22 bits
-        // come from two fixed 11-bit digit passes instead, the sample's
-        // largest key noted on the first; sm.smax is zero on entry (set at
-        // the kernel's start; the sampler wave sets it itself later).
-        uint32_t smax = 0u;
-        constexpr int kTopShift = 32 - kDigitBits;
-        each_key([&](uint32_t key) {
-            smax = max(smax, key);
-            if (want > 0u) atomicAdd(&lds.hist[key >> kTopShift], 1u);
-        });
-        smax = wave_max(smax);
-        if (lane_id() == 0) atomicMax(&sm.smax, smax);
+        // The whole workgroup (row 0): every lane holds at most 4 kPer keys,
+        // too few for a per-lane bound. A bound per wave instead: each wave
+        // takes qw = ceil(want / waves) and finds the qw-th largest of its
+        // lanes' maxima, bit by bit from the top with one ballot per bit (no
+        // LDS traffic), so that at least qw of the wave's keys lie at or
+        // above it; the smallest over the waves, lo, has at least want keys
+        // at or above it. The keys in [lo, sample max] are then narrowed as
+        // the one-wave search below narrows them.
+        constexpr uint32_t kWaves = S::kSize / 64;
+        uint32_t key[4 * kPer];
+        uint32_t valid = 0u, lmax = 0u;
+#pragma unroll
+        for (int h = 0; h < kPer; ++h) {
+            const int t = h * S::kSize + (int)S::rank();
+            uint4 g = make_uint4(0u, 0u, 0u, 0u);
+            if (t < nsv) {
+                g = *reinterpret_cast<const uint4*>(sm.skey + 4 * t);
+                valid |= 0xFu << (4 * h);
+            }
+            key[4 * h + 0] = order_key(__uint_as_float(g.x));
+            key[4 * h + 1] = order_key(__uint_as_float(g.y));
+            key[4 * h + 2] = order_key(__uint_as_float(g.z));
+            key[4 * h + 3] = order_key(__uint_as_float(g.w));
+        }
+#pragma unroll
+        for (int j = 0; j < 4 * kPer; ++j) lmax = max(lmax, (valid >> j) & 1u ? key[j] : 0u);
+        const uint32_t hi_w = wave_max(lmax);
+        uint32_t lo_w = 0u;
+        const uint32_t qw = (want + kWaves - 1u) / kWaves;
+        if (want > 0u && qw <= 64u) {
+            // the largest v with at least qw lane maxima at or above it
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t c = lo_w | (1u << bit);
+                if ((uint32_t)__popcll(__ballot(lmax >= c)) >= qw) lo_w = c;
+            }
+        }
+        if (lane_id() == 0) {
+            sm.cand_key[wave_id()] = lo_w;
+            sm.cand_idx[wave_id()] = hi_w;
+        }
         S::sync();
+        // one lane reads the waves' bounds (the other lanes' reads would
+        // cost LDS bandwidth), and shares them
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+        if (lane_id() == 0) {
+#pragma unroll
+            for (uint32_t w = 0; w < kWaves; ++w) {
+                lo = min(lo, sm.cand_key[w]);
+                hi = max(hi, sm.cand_idx[w]);
+            }
+        }
+        lo = __builtin_amdgcn_readfirstlane(lo);
+        hi = __builtin_amdgcn_readfirstlane(hi);
         uint32_t T = 0u;  // too short to sample, or want out of reach: keep everything
         if (want > 0u) {
-            const Found f1 = find_rank_bin<S>(lds, want);
-            each_key([&](uint32_t key) {
-                if ((key >> kTopShift) == f1.digit) atomicAdd(&lds.hist[(key >> kFine) & (kBins - 1)], 1u);
-            });
-            S::sync();
-            const Found f2 = find_rank_bin<S>(lds, want - f1.above);
-            T = (f1.digit << kTopShift) | (f2.digit << kFine);
+            uint32_t base = lo, top = hi, rank = want;
+            for (;;) {
+                const uint32_t span = top - base;
+                const int wb = span == 0u ? 0 : 32 - __clz(span);
+                const int sh = wb > kDigitBits ? wb - kDigitBits : 0;  // span >> sh < 2048
+#pragma unroll
+                for (int j = 0; j < 4 * kPer; ++j) {
+                    const uint32_t k = key[j];
+                    if (((valid >> j) & 1u) && k >= base && k <= top) atomicAdd(&lds.hist[(k - base) >> sh], 1u);
+                }
+                S::sync();
+                const Found f = find_rank_bin<S>(lds, rank);
+                const uint32_t edge = base + (f.digit << sh);
+                if (sh <= kFineShift) {
+                    T = edge;
+                    break;
+                }
+                rank -= f.above;
+                const uint32_t room = top - edge;
+                top = edge + (room < (1u << sh) - 1u ? room : (1u << sh) - 1u);
+                base = edge;
+            }
         }
-        const uint32_t span = sm.smax - T;
+        const uint32_t span = hi - T;
         const int wbits = span == 0u ? 0 : 32 - __clz(span);
         if (S::rank() == 0) {
             R.T = T;
@@ -702,12 +761,6 @@ struct SampleRegs {
         }
     }
 };
-
-template <class S>
-__device__ __forceinline__ void sample_cutoff(const Params& p, Shared& sm, RowSlot& R, SelectLds lds) {
-    sample_load<S>(p, sm, R);
-    sample_select<S>(sm, R, lds);
-}
 
 // ----------------------------------------------------------------------------
 // progress counters between the roles
@@ -848,6 +901,7 @@ struct Streamer {
     int ok;      // rows up to this one have their cutoff set and their buffer free
     uint32_t T, buf;
     int64_t L;
+    uint32_t pre = kNone;  // a second chunk of row i issued at the start, into the other registers
 
     __device__ __forceinline__ void leave(int r) { publish_add(&sm.left[r % kSlots], 1u); }
 
@@ -972,8 +1026,13 @@ struct Streamer {
     // then filter `held`. False when this workgroup's rows are done.
     __device__ __forceinline__ bool step(Chunk& held, Chunk& next) {
         int r = i;
-        uint32_t cn = grab(r, i + 2, true);
-        load(next, r, cn);
+        uint32_t cn = pre;
+        if (cn < kNone) {
+            pre = kNone;
+        } else {
+            cn = grab(r, i + 2, true);
+            load(next, r, cn);
+        }
         if (!filter_held(held)) {
             // over capacity: no wave takes more of this row
             if (lane_id() == 0) atomicMax(&sm.chunk_next[i % kSlots], nchunks(sm.slot[i % kSlots]));
@@ -1334,7 +1393,6 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         sm.ncand = 0u;
         sm.ndeferred = 0u;
         sm.ndirect = 0u;
-        sm.nheavy = 0u;
         sm.nrank = 0u;
         sm.smax = 0u;
         sm.take_cand = 0u;
@@ -1352,13 +1410,13 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     const SelectLds sampler_lds{sm.shist, sm.sfound};
 
     // start. Workgroup w's first row is row w in every queue layout, so it
-    // is known before the queue is built: its sample's loads go out before
-    // the length sort, whose time they overlap. Once the queue is built, the
-    // sampler wave claims the next row, each streaming wave issues a chunk of
-    // row 0 (issued earlier, the chunks' loads, 80 KB per compute unit,
-    // delay the sample's and slow the sort), the whole workgroup finds row
-    // 0's cutoff from the sample while they are in flight, and the roles
-    // start.
+    // is known before the queue is built: its sample's loads go out first,
+    // then each streaming wave's first two chunks of it (160 KB per compute
+    // unit), and the whole workgroup finds row 0's cutoff from the sample
+    // while the chunks are in flight. An ordered queue is only counted
+    // here; the sampler wave makes its table once the roles start (while
+    // row 0 streams) and claims the next rows. Otherwise the queue is dealt
+    // first and the sampler wave claims the next row before the roles start.
     const int64_t b0 = blockIdx.x;  // the grid is min(batch, CUs)
     // every length load in flight before the first is used
     const bool ordered = p.batch > (int64_t)gridDim.x && queue_ordered(p.batch);
@@ -1387,58 +1445,83 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     // length loads: one row per workgroup, or the ordered queue.
     const bool early = stream0 && (ordered || p.batch <= (int64_t)gridDim.x);
     const bool sampled0 = early && kind0 == kKindSampled;
+    const bool queue_later = ordered;  // the table is made by the sampler wave once the roles start
     SampleRegs<B> sample;
     if (sampled0) sample.issue(p, b0, L0);
-    Chunk a, b;
-    Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0};
     if (stream0 && threadIdx.x == 0) {
         fill_slot(sm.slot[0], p, b0, L0, kind0);
-        sm.chunk_next[0] = early ? (uint32_t)kStreamers : 0u;
+        sm.chunk_next[0] = early ? 2u * (uint32_t)kStreamers : 0u;
     }
-    build_queue(p, sm, L0, lens);
-    if (wave_id() == 1) {
-        if (L0 > p.k && kind0 == kKindFull) defer_row(p, sm, sampler_lds, &sm.semitted, b0, TOPK_ROW_FULL_FORCED);
-        if (!stream0) claim_row(p, sm, sm.slot[0], sampler_lds, &sm.semitted);
-        claim_row(p, sm, sm.slot[1], sampler_lds, &sm.semitted);
-        if (lane_id() == 0) sm.n_claimed = 2u;
+    if (queue_later) {
+        queue_count(p, sm, queue_lds(sm), L0, lens);
+        if (threadIdx.x == 0) sm.n_claimed = stream0 ? 1u : 0u;
+        if (wave_id() == 1 && L0 > p.k && kind0 == kKindFull)
+            defer_row(p, sm, sampler_lds, &sm.semitted, b0, TOPK_ROW_FULL_FORCED);
+    } else {
+        build_queue(p, sm, L0);
+        if (wave_id() == 1) {
+            if (L0 > p.k && kind0 == kKindFull) defer_row(p, sm, sampler_lds, &sm.semitted, b0, TOPK_ROW_FULL_FORCED);
+            if (!stream0) claim_row(p, sm, sm.slot[0], sampler_lds, &sm.semitted);
+            claim_row(p, sm, sm.slot[1], sampler_lds, &sm.semitted);
+            if (lane_id() == 0) sm.n_claimed = 2u;
+        }
     }
     if (sampled0) sample.store(sm, L0);
     B::sync();
-    // Row 0 when it comes after the queue (row w of a batch dealt in index
-    // order, or the queue's first row when row w was written directly or
-    // deferred): its sample, then its chunks.
+    Chunk a, b;
+    Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0};
+    if (early && wave_id() >= kFirstStreamer) {
+        // Each streaming wave's first two chunks of row 0, from one load
+        // site each (their registers then stay where the roles use them):
+        // streaming wave s takes chunks s and s + kStreamers, and a wave
+        // left without its first is done with row 0. Chunks past the row
+        // issue loads that touch no memory. Only streaming waves load here:
+        // a wave that issues loads waits until the compute unit's memory
+        // queue takes them.
+        const uint32_t c0 = wave_id() - kFirstStreamer;
+        const uint32_t nc0 = nchunks_of(L0);
+        const uint32_t c = c0 < nc0 ? c0 : kNone;
+        const uint32_t c1 = c0 + kStreamers < nc0 ? c0 + kStreamers : kNone;
+        const float* row0 = p.scores + b0 * p.row_stride;
+        load_chunk(a, c < kNone ? row0 : p.scores, c < kNone ? L0 : 0, c);
+        load_chunk(b, c1 < kNone ? row0 : p.scores, c1 < kNone ? L0 : 0, c1);
+        st.c = c;
+        st.pre = c1;
+        if (c == kNone) {
+            st.leave(0);
+            st.i = 1;
+        }
+    }
+    // Row 0 when it comes after a queue dealt in index order: its sample,
+    // then its chunks.
     const bool late = !early && sm.slot[0].valid;
     const bool late_sampled = late && sm.slot[0].kind == kKindSampled;
     if (late_sampled) sample_load<B>(p, sm, sm.slot[0]);
-    {
-        // Each streaming wave's first chunk, from one load site (its
-        // registers then stay where the roles use them, and nothing waits
-        // for them before the roles start). Row 0 from the start: streaming
-        // wave s takes chunk s, a wave left without one is done with row 0.
-        // After the queue: the next chunk of rows 0-1 (later rows are not
-        // claimed yet). Waves without a chunk issue loads that touch no
-        // memory.
-        const bool streamer = wave_id() >= kFirstStreamer;
-        uint32_t c = kNone;
-        if (streamer && early) {
-            const uint32_t c0 = wave_id() - kFirstStreamer;
-            if (c0 < nchunks_of(L0)) {
-                c = c0;
-            } else {
-                st.leave(0);
-                st.i = 1;
-            }
-        } else if (streamer && late) {
-            c = st.grab(st.i, 1, false);
-        }
-        const RowSlot& R = sm.slot[(c < kNone ? st.i : 0) % kSlots];
-        load_chunk(a, c < kNone ? p.scores + R.b * p.row_stride : p.scores, c < kNone ? R.L : 0, c);
-        st.c = c;
+    if (late && wave_id() >= kFirstStreamer) {
+        // after the queue: each streaming wave's first chunk of rows 0-1
+        // (later rows are not claimed yet)
+        st.c = st.grab(st.i, 1, false);
+        if (st.c < kNone) st.load(a, st.i, st.c);
     }
-    if (late_sampled) B::sync();
-    if (sampled0 || late_sampled) sample_select<B>(sm, sm.slot[0], sampler_lds);
-    if (threadIdx.x == 0) sm.n_ready = 1u;
-    B::sync();
+    if (late_sampled) {
+        B::sync();
+        sample_select<B>(sm, sm.slot[0], sampler_lds);
+    }
+    if (sampled0) {
+        // row 0's cutoff from the sample by the sampler wave alone, while the
+        // streaming waves issue their chunks' loads (a wave that issues
+        // loads waits until the compute unit's memory queue takes them, so
+        // a cutoff found by the whole workgroup would wait for the queue)
+        if (wave_id() == 1) {
+            sample_select<WaveScope>(sm, sm.slot[0], sampler_lds);
+            publish(&sm.n_ready, 1u);
+        }
+    } else {
+        // row 0's cutoff is set (or there is no row 0), unless the sampler
+        // wave is still to claim it from the table
+        if (threadIdx.x == 0 && (stream0 || !queue_later)) sm.n_ready = 1u;
+        B::sync();
+    }
 
     if (wave_id() == 0) {
         // finisher: rows in order; the last row is left to the whole workgroup
@@ -1463,12 +1546,46 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         }
         if (lane_id() == 0) sm.last_row = last;
     } else if (wave_id() == 1) {
-        // sampler: the cutoff of row j, then the claim of row j + 1, whose
-        // slot held row j - 3
+        // sampler: the queue's table if it is still to make, the claim of
+        // rows 1 (and 0, if row w was not streamed) and that row 0's cutoff;
+        // then the cutoff of row j, and the claim of row j + 1, whose slot
+        // held row j - 3
+        // The next row's sample goes out as soon as the table's first row is
+        // known (its loads wait behind the streaming waves' loads); the row
+        // claimed from the table is that row unless it is deferred.
+        int64_t issued = -1;  // the row whose sample is in flight
+        if (queue_later) {
+            queue_table(p, sm, queue_lds(sm), [&](int64_t b, int64_t L) {
+                if (row_kind(p, L) != kKindSampled) return;
+                RowSlot R;
+                R.b = b;
+                R.L = L;
+                sample_issue<WaveScope>(p, sm, R);
+                issued = b;
+            });
+            if (!stream0) claim_row(p, sm, sm.slot[0], sampler_lds, &sm.semitted);
+            claim_row(p, sm, sm.slot[1], sampler_lds, &sm.semitted);
+            publish(&sm.n_claimed, 2u);
+            if (!stream0) {
+                RowSlot& R0 = sm.slot[0];
+                if (R0.valid && R0.kind == kKindSampled) {
+                    if (R0.b != issued) sample_issue<WaveScope>(p, sm, R0);
+                    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                    sample_select<WaveScope>(sm, R0, sampler_lds);
+                    issued = -1;
+                }
+                publish(&sm.n_ready, 1u);
+            }
+        }
         for (int j = 1;; ++j) {
             const int s = j % kSlots;
             if (!sm.slot[s].valid) break;
-            if (sm.slot[s].kind == kKindSampled) sample_cutoff<WaveScope>(p, sm, sm.slot[s], sampler_lds);
+            if (sm.slot[s].kind == kKindSampled) {
+                if (sm.slot[s].b != issued) sample_issue<WaveScope>(p, sm, sm.slot[s]);
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                sample_select<WaveScope>(sm, sm.slot[s], sampler_lds);
+                issued = -1;
+            }
             publish(&sm.n_ready, (uint32_t)j + 1u);
             if (j >= 3 && !wait_for(sm, &sm.n_finished, (uint32_t)j - 2u)) break;
             const int sn = (j + 1) % kSlots;

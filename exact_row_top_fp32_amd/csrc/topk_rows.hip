@@ -58,6 +58,7 @@ constexpr int kRunLen = 64;                                // floats per contigu
 constexpr int kMaxRuns = 64;                               // runs per sample
 constexpr int kMaxSample = kMaxRuns * kRunLen;             // 4096 keys at most
 constexpr int kFineShift = 14;                             // T to within 2^14 keys (1/512 octave)
+constexpr int kPairFineShift = 16;                         // row 0's T: to within 2^16 keys (1/128 octave)
 constexpr int kSlots = 4;                                  // rows i-1 .. i+2
 constexpr int kTable = 64;                                 // queued rows fetched at a time
 constexpr int kMaxDeferred = 64;                           // full-row rows per workgroup
@@ -93,6 +94,7 @@ struct RowSlot {
     uint32_t sh;
     uint32_t kind;
     uint32_t valid;
+    uint32_t nsv;  // 4-score groups in the row's sample, when sampled
 };
 
 struct Shared {
@@ -115,10 +117,9 @@ struct Shared {
     uint32_t emitted;             // output slots, finisher and whole workgroup
     uint32_t semitted;            // output slots, sampler
     uint32_t ncand;
-    uint32_t smax;
-    uint32_t slo;
     alignas(16) uint32_t cand_key[kMaxCand];
     alignas(16) uint32_t cand_idx[kMaxCand];
+    uint32_t pair;       // row 0's cutoff by waves 0 and 1: bounds posted, then halves counted
     uint32_t take_cand;  // the last row's slots: taken (low 16 bits) and candidates (high 16)
     uint32_t ndeferred;
     int32_t deferred[kMaxDeferred];
@@ -434,6 +435,41 @@ __device__ __forceinline__ void fill_table(const Params& p, Shared& sm) {
     WaveScope::sync();
 }
 
+// Where a row's sample lies: `runs` runs of kRunLen scores; run r starts at
+// floor(r (L - 64) / (runs - 1)) rounded down to a multiple of 4.
+struct SamplePlan {
+    int runs;
+    int nsv;  // 4-score groups in the sample
+    int64_t step_q;
+    uint32_t step_r;
+    __device__ __forceinline__ explicit SamplePlan(int64_t L) {
+        const int64_t fit = L / (2 * kRunLen);
+        runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
+        nsv = runs >= 2 ? runs * (kRunLen / 4) : 0;
+        const int64_t span = runs >= 2 ? (L - kRunLen) : 0;
+        step_q = runs >= 2 ? span / (runs - 1) : 0;
+        step_r = runs >= 2 ? (uint32_t)(span - step_q * (runs - 1)) : 0u;
+    }
+    __device__ __forceinline__ int64_t run_start(int r) const {
+        return ((int64_t)r * step_q + (int64_t)(((uint32_t)r * step_r) / (uint32_t)(runs - 1))) & ~(int64_t)3;
+    }
+    // first score of 4-score group t of the sample
+    __device__ __forceinline__ int64_t group_start(int t) const {
+        return run_start(t / (kRunLen / 4)) + 4 * (t % (kRunLen / 4));
+    }
+    // runs that lie wholly in [0, L): a leading run of them, as the starts grow
+    __device__ __forceinline__ int runs_within(int64_t L) const {
+        if (runs < 2) return 0;
+        int lo = 0, hi = runs;  // run_start(r) + kRunLen <= L for r < lo, not for r >= hi
+        while (lo < hi) {
+            const int mid = (lo + hi) / 2;
+            if (run_start(mid) + kRunLen <= L) lo = mid + 1;
+            else hi = mid;
+        }
+        return lo;
+    }
+};
+
 // How a row with L > k is selected: every key kept (L within the capacity),
 // sampled, or the full-row path, as the caller's forced path allows.
 __device__ __forceinline__ uint32_t row_kind(const Params& p, int64_t L) {
@@ -452,6 +488,7 @@ __device__ __forceinline__ void fill_slot(RowSlot& slot, const Params& p, int64_
     slot.sh = 32 - kDigitBits;  // and bins take the top 11 bits
     slot.kind = kind;
     slot.valid = 1u;
+    slot.nsv = (uint32_t)SamplePlan(L).nsv;
 }
 
 // One wave: this workgroup's next row into `slot` (invalid once its share is
@@ -500,30 +537,6 @@ __device__ __forceinline__ void claim_row(const Params& p, Shared& sm, RowSlot& 
 // narrowed by further histograms until bins are at most 2^kFineShift keys
 // wide, and T is the lower edge of the last bin. The bin width of the
 // survivor histogram makes [T, sample max] cover about half its bins.
-//
-// Where a row's sample lies: `runs` runs of kRunLen scores; run r starts at
-// floor(r (L - 64) / (runs - 1)) rounded down to a multiple of 4.
-struct SamplePlan {
-    int runs;
-    int nsv;  // 4-score groups in the sample
-    int64_t step_q;
-    uint32_t step_r;
-    __device__ __forceinline__ explicit SamplePlan(int64_t L) {
-        const int64_t fit = L / (2 * kRunLen);
-        runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
-        nsv = runs >= 2 ? runs * (kRunLen / 4) : 0;
-        const int64_t span = runs >= 2 ? (L - kRunLen) : 0;
-        step_q = runs >= 2 ? span / (runs - 1) : 0;
-        step_r = runs >= 2 ? (uint32_t)(span - step_q * (runs - 1)) : 0u;
-    }
-    // first score of 4-score group t of the sample
-    __device__ __forceinline__ int64_t group_start(int t) const {
-        const int r = t / (kRunLen / 4);
-        const int64_t start =
-            ((int64_t)r * step_q + (int64_t)(((uint32_t)r * step_r) / (uint32_t)(runs - 1))) & ~(int64_t)3;
-        return start + 4 * (t % (kRunLen / 4));
-    }
-};
 
 // Scope S: issues the loads of row R's sample from HBM straight into LDS,
 // group t at skey[4t, 4t + 4) whichever scope loads it (lane l of a wave
@@ -558,58 +571,103 @@ __device__ __forceinline__ void sample_load(const Params& p, Shared& sm, const R
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
-// Scope S: the cutoff of row R from the sample in LDS.
+// How many of the sample's keys the cutoff keeps at or above it (0: every
+// key, the sample being too small for the rule): with n keys from a row of
+// L, the count above the row's m-th largest key has mean mu = m n / L, and
+// want sits 6 standard deviations (sqrt(mu)) and 4 keys above it.
+__device__ __forceinline__ uint32_t sample_want(const RowSlot& R) {
+    const uint32_t n = R.nsv * 4u;
+    const float mu = (float)R.m * (float)n / (float)R.L;
+    const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
+    return wantf < (float)n ? (uint32_t)wantf : 0u;
+}
+
+// Waves 0 and 1 together, wave w (row 0 at start, when neither has chunk
+// loads of its own in flight): the loads of a sample laid out by `plan`
+// from row b straight into LDS, groups h 128 + 64 w + lane.
+__device__ __forceinline__ void sample_issue_pair(const Params& p, Shared& sm, int64_t b, const SamplePlan& plan,
+                                                  uint32_t w) {
+    constexpr int kPer = kMaxSample / 4 / 128;  // 16-byte loads per lane
+    const float* row = p.scores + b * p.row_stride;
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+        const int t = h * 128 + (int)(64u * w);
+        if (t + (int)lane_id() < plan.nsv)
+            __builtin_amdgcn_global_load_lds(row + plan.group_start(t + (int)lane_id()),
+                                             (__attribute__((address_space(3))) void*)(sm.skey + 4 * t), 16, 0, 0);
+    }
+}
+
+// Scope S: the cutoff of row R from the sample in LDS. The bound lo: with
+// one wave, each lane keeps the q = ceil(want / 64) largest of its 4-key
+// groups' maxima, and lo is the smallest of the lanes' q-th largest (each
+// lane has q distinct keys at or above it; lo = 0 when q is too large to
+// keep); with the whole workgroup, whose lanes hold a few keys each, each
+// wave takes qw = ceil(want / waves) and finds the qw-th largest of its
+// lanes' maxima, bit by bit from the top with one ballot per bit, and lo is
+// the smallest over the waves. Either way at least want keys lie in
+// [lo, sample max]. The workgroup's lanes hold their keys in registers for
+// every pass; one wave reads its 64 keys per lane from LDS in each pass.
 template <class S>
 __device__ __forceinline__ void sample_select(Shared& sm, RowSlot& R, SelectLds lds) {
-    constexpr int kPer = (kMaxSample / 4 + S::kSize - 1) / S::kSize;  // groups per lane
-    constexpr int kQ = 4;                                              // most keys kept per lane
-    const int64_t L = R.L;
-    const int nsv = SamplePlan(L).nsv;
-    const uint32_t n = (uint32_t)nsv * 4;
-    const float mu = (float)R.m * (float)n / (float)L;
-    const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
-    const uint32_t want = wantf < (float)n ? (uint32_t)wantf : 0u;  // 0: keep every key
-    const uint32_t q = (want + S::kSize - 1) / S::kSize;
+    constexpr int kPer = (kMaxSample / 4 + S::kSize - 1) / S::kSize;  // 4-key groups per lane
+    constexpr uint32_t kWaves = S::kSize / 64;
+    constexpr bool kHeld = kWaves > 1;  // keys held in registers
+    constexpr int kQ = 4;               // largest group maxima kept per lane (one wave)
+    const int nsv = (int)R.nsv;
+    const uint32_t want = sample_want(R);
+    auto group = [&](int h) -> uint4 {  // group h of this lane's keys (zero keys outside the sample)
+        const int t = h * S::kSize + (int)S::rank();
+        uint4 k = make_uint4(0u, 0u, 0u, 0u);
+        if (t < nsv) {
+            const uint4 g = *reinterpret_cast<const uint4*>(sm.skey + 4 * t);
+            k = make_uint4(order_key(__uint_as_float(g.x)), order_key(__uint_as_float(g.y)),
+                           order_key(__uint_as_float(g.z)), order_key(__uint_as_float(g.w)));
+        }
+        return k;
+    };
+    uint4 held[kHeld ? kPer : 1];
+    if constexpr (kHeld) {
+#pragma unroll
+        for (int h = 0; h < kPer; ++h) held[h] = group(h);
+    }
+    // f(key) for every key of this lane in the sample
     auto each_key = [&](auto&& f) {
-#pragma unroll 4
+#pragma unroll
         for (int h = 0; h < kPer; ++h) {
-            const int t = h * S::kSize + (int)S::rank();
-            if (t < nsv) {
-                const uint4 g = *reinterpret_cast<const uint4*>(sm.skey + 4 * t);
-                f(order_key(__uint_as_float(g.x)));
-                f(order_key(__uint_as_float(g.y)));
-                f(order_key(__uint_as_float(g.z)));
-                f(order_key(__uint_as_float(g.w)));
-            }
+            if (h * S::kSize + (int)S::rank() >= nsv) continue;
+            uint4 k;
+            if constexpr (kHeld) k = held[h];
+            else k = group(h);
+            f(k.x);
+            f(k.y);
+            f(k.z);
+            f(k.w);
         }
     };
-    if constexpr (S::kSize > 64) {
-        // The whole workgroup (row 0): every lane holds at most 4 kPer keys,
-        // too few for a per-lane bound. A bound per wave instead: each wave
-        // takes qw = ceil(want / waves) and finds the qw-th largest of its
-        // lanes' maxima, bit by bit from the top with one ballot per bit (no
-        // LDS traffic), so that at least qw of the wave's keys lie at or
-        // above it; the smallest over the waves, lo, has at least want keys
-        // at or above it. The keys in [lo, sample max] are then narrowed as
-        // the one-wave search below narrows them.
-        constexpr uint32_t kWaves = S::kSize / 64;
-        uint32_t key[4 * kPer];
-        uint32_t valid = 0u, lmax = 0u;
+    uint32_t lo = 0u, hi = 0u;
+    if constexpr (!kHeld) {
+        const uint32_t q = (want + 63u) / 64u;
+        uint32_t top[kQ] = {0u, 0u, 0u, 0u};  // the lane's largest group maxima, descending
 #pragma unroll
         for (int h = 0; h < kPer; ++h) {
-            const int t = h * S::kSize + (int)S::rank();
-            uint4 g = make_uint4(0u, 0u, 0u, 0u);
-            if (t < nsv) {
-                g = *reinterpret_cast<const uint4*>(sm.skey + 4 * t);
-                valid |= 0xFu << (4 * h);
-            }
-            key[4 * h + 0] = order_key(__uint_as_float(g.x));
-            key[4 * h + 1] = order_key(__uint_as_float(g.y));
-            key[4 * h + 2] = order_key(__uint_as_float(g.z));
-            key[4 * h + 3] = order_key(__uint_as_float(g.w));
-        }
+            const uint4 k = group(h);
+            uint32_t v = max(max(k.x, k.y), max(k.z, k.w));  // 0 outside the sample
 #pragma unroll
-        for (int j = 0; j < 4 * kPer; ++j) lmax = max(lmax, (valid >> j) & 1u ? key[j] : 0u);
+            for (int j = 0; j < kQ; ++j) {
+                const uint32_t up = max(top[j], v);
+                v = min(top[j], v);
+                top[j] = up;
+            }
+        }
+        uint32_t mine = 0u;
+#pragma unroll
+        for (int j = 0; j < kQ; ++j) mine = (uint32_t)(j + 1) == q ? top[j] : mine;
+        lo = q >= 1u && q <= (uint32_t)kQ ? wave_min(mine) : 0u;
+        hi = wave_max(top[0]);
+    } else {
+        uint32_t lmax = 0u;
+        each_key([&](uint32_t k) { lmax = max(lmax, k); });
         const uint32_t hi_w = wave_max(lmax);
         uint32_t lo_w = 0u;
         const uint32_t qw = (want + kWaves - 1u) / kWaves;
@@ -627,7 +685,7 @@ __device__ __forceinline__ void sample_select(Shared& sm, RowSlot& R, SelectLds 
         S::sync();
         // one lane reads the waves' bounds (the other lanes' reads would
         // cost LDS bandwidth), and shares them
-        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+        lo = 0xFFFFFFFFu;
         if (lane_id() == 0) {
 #pragma unroll
             for (uint32_t w = 0; w < kWaves; ++w) {
@@ -637,79 +695,18 @@ __device__ __forceinline__ void sample_select(Shared& sm, RowSlot& R, SelectLds 
         }
         lo = __builtin_amdgcn_readfirstlane(lo);
         hi = __builtin_amdgcn_readfirstlane(hi);
-        uint32_t T = 0u;  // too short to sample, or want out of reach: keep everything
-        if (want > 0u) {
-            uint32_t base = lo, top = hi, rank = want;
-            for (;;) {
-                const uint32_t span = top - base;
-                const int wb = span == 0u ? 0 : 32 - __clz(span);
-                const int sh = wb > kDigitBits ? wb - kDigitBits : 0;  // span >> sh < 2048
-#pragma unroll
-                for (int j = 0; j < 4 * kPer; ++j) {
-                    const uint32_t k = key[j];
-                    if (((valid >> j) & 1u) && k >= base && k <= top) atomicAdd(&lds.hist[(k - base) >> sh], 1u);
-                }
-                S::sync();
-                const Found f = find_rank_bin<S>(lds, rank);
-                const uint32_t edge = base + (f.digit << sh);
-                if (sh <= kFineShift) {
-                    T = edge;
-                    break;
-                }
-                rank -= f.above;
-                const uint32_t room = top - edge;
-                top = edge + (room < (1u << sh) - 1u ? room : (1u << sh) - 1u);
-                base = edge;
-            }
-        }
-        const uint32_t span = hi - T;
-        const int wbits = span == 0u ? 0 : 32 - __clz(span);
-        if (S::rank() == 0) {
-            R.T = T;
-            R.sh = (uint32_t)(wbits > kDigitBits - 1 ? wbits - (kDigitBits - 1) : 0);
-        }
-        S::sync();
-        return;
     }
-    uint32_t top[kQ] = {0u, 0u, 0u, 0u};  // this lane's largest keys, descending
-    uint32_t smax = 0u;
-    each_key([&](uint32_t key) {
-        smax = max(smax, key);
-#pragma unroll
-        for (int j = 0; j < kQ; ++j) {
-            const uint32_t hi = max(top[j], key);
-            key = min(top[j], key);
-            top[j] = hi;
-        }
-    });
-    uint32_t lo = 0u;
-#pragma unroll
-    for (int j = 0; j < kQ; ++j) lo = (uint32_t)(j + 1) == q ? top[j] : lo;
-    lo = wave_min(lo);
-    smax = wave_max(smax);
-    if (S::rank() == 0) {
-        sm.smax = 0u;
-        sm.slo = 0xFFFFFFFFu;
-    }
-    S::sync();
-    if (lane_id() == 0) {
-        atomicMax(&sm.smax, smax);
-        atomicMin(&sm.slo, lo);
-    }
-    S::sync();
-    const uint32_t hi = sm.smax;
-    lo = sm.slo;
     uint32_t T = 0u;  // too short to sample, or want out of reach: keep everything
-    if (want > 0) {
+    if (want > 0u) {
         // the rank-th largest key in [base, top] lies in one of 2048 bins of
         // width 2^sh; narrow to that bin until bins are fine enough
-        uint32_t base = q > (uint32_t)kQ ? 0u : lo, top = hi, rank = want;
+        uint32_t base = lo, top = hi, rank = want;
         for (;;) {
             const uint32_t span = top - base;
             const int wb = span == 0u ? 0 : 32 - __clz(span);
             const int sh = wb > kDigitBits ? wb - kDigitBits : 0;  // span >> sh < 2048
-            each_key([&](uint32_t key) {
-                if (key >= base && key <= top) atomicAdd(&lds.hist[(key - base) >> sh], 1u);
+            each_key([&](uint32_t k) {
+                if (k >= base && k <= top) atomicAdd(&lds.hist[(k - base) >> sh], 1u);
             });
             S::sync();
             const Found f = find_rank_bin<S>(lds, rank);
@@ -733,34 +730,7 @@ __device__ __forceinline__ void sample_select(Shared& sm, RowSlot& R, SelectLds 
     S::sync();
 }
 
-// Scope S: a row's sample through registers, for the first row, whose
-// loads are issued while other loads of the same waves are still to come:
-// the compiler then waits for exactly the sample's loads where it stores
-// them to LDS (group t at skey[4t, 4t + 4), as sample_issue places it).
-template <class S>
-struct SampleRegs {
-    static constexpr int kPer = (kMaxSample / 4 + S::kSize - 1) / S::kSize;  // groups per lane
-    f4 v[kPer];
-    __device__ __forceinline__ void issue(const Params& p, int64_t b, int64_t L) {
-        const SamplePlan plan(L);
-        const float* row = p.scores + b * p.row_stride;
-#pragma unroll
-        for (int h = 0; h < kPer; ++h) {
-            const int t = h * S::kSize + (int)S::rank();
-            if (t < plan.nsv) v[h] = *reinterpret_cast<const f4*>(row + plan.group_start(t));
-        }
-    }
-    __device__ __forceinline__ void store(Shared& sm, int64_t L) const {
-        const int nsv = SamplePlan(L).nsv;
-#pragma unroll
-        for (int h = 0; h < kPer; ++h) {
-            const int t = h * S::kSize + (int)S::rank();
-            if (t < nsv)
-                *reinterpret_cast<uint4*>(sm.skey + 4 * t) = make_uint4(
-                    __float_as_uint(v[h].x), __float_as_uint(v[h].y), __float_as_uint(v[h].z), __float_as_uint(v[h].w));
-        }
-    }
-};
+
 
 // ----------------------------------------------------------------------------
 // progress counters between the roles
@@ -812,6 +782,132 @@ __device__ __forceinline__ bool wait_for(Shared& sm, const uint32_t* ctr, uint32
         }
         __builtin_amdgcn_s_sleep(1);
     }
+}
+
+// Waves 0 and 1 together, wave w: the cutoff of row R from its sample in LDS
+// (groups [0, R.nsv), wave w reading groups h 128 + 64 w + lane, its keys
+// held in registers). Each wave bounds its half as one wave does
+// (q = ceil(want / 128)), the two bounds are exchanged through LDS and a
+// counter, each wave adds its half's keys in [lo, sample max] to a 1024-bin
+// histogram, and the wave that finishes second finds the want-th largest
+// key's bin with one prefix sum (each lane summing 16 bins) and publishes
+// the bin's lower edge as the cutoff (n_ready = 1); when that bin is wider
+// than 2^kPairFineShift keys, the whole search by one wave instead. Returns
+// whether this wave published.
+__device__ __forceinline__ bool sample_select_pair(Shared& sm, RowSlot& R, SelectLds lds, uint32_t w) {
+    constexpr int kPer = kMaxSample / 4 / 128;  // 4-key groups per lane
+    constexpr int kQ = 4;
+    constexpr int kPairBits = 10;  // 1024 bins, 16 per lane
+    const int nsv = (int)R.nsv;
+    const uint32_t want = sample_want(R);
+    const uint32_t lane = lane_id();
+    uint4 key[kPer];
+    uint32_t gvalid = 0u;
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+        const int t = h * 128 + (int)(64u * w + lane);
+        uint4 k = make_uint4(0u, 0u, 0u, 0u);
+        if (t < nsv) {
+            const uint4 g = *reinterpret_cast<const uint4*>(sm.skey + 4 * t);
+            k = make_uint4(order_key(__uint_as_float(g.x)), order_key(__uint_as_float(g.y)),
+                           order_key(__uint_as_float(g.z)), order_key(__uint_as_float(g.w)));
+            gvalid |= 1u << h;
+        }
+        key[h] = k;
+    }
+    const uint32_t q = (want + 127u) / 128u;
+    uint32_t top[kQ] = {0u, 0u, 0u, 0u};  // the lane's largest group maxima, descending
+#pragma unroll
+    for (int h = 0; h < kPer; ++h) {
+        uint32_t v = max(max(key[h].x, key[h].y), max(key[h].z, key[h].w));  // 0 outside the sample
+#pragma unroll
+        for (int j = 0; j < kQ; ++j) {
+            const uint32_t up = max(top[j], v);
+            v = min(top[j], v);
+            top[j] = up;
+        }
+    }
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) mine = (uint32_t)(j + 1) == q ? top[j] : mine;
+    const uint32_t lo_w = q >= 1u && q <= (uint32_t)kQ ? wave_min(mine) : 0u;
+    const uint32_t hi_w = wave_max(top[0]);
+    if (lane == 0) {
+        sm.cand_key[w] = lo_w;
+        sm.cand_idx[w] = hi_w;
+    }
+    publish_add(&sm.pair, 1u);
+    if (!wait_for(sm, &sm.pair, 2u)) return false;
+    const uint32_t lo = min(sm.cand_key[0], sm.cand_key[1]);
+    const uint32_t hi = max(sm.cand_idx[0], sm.cand_idx[1]);
+    const uint32_t span = hi - lo;
+    const int wb = span == 0u ? 0 : 32 - __clz(span);
+    const int sh = wb > kPairBits ? wb - kPairBits : 0;  // span >> sh < 1024
+    if (want > 0u) {
+#pragma unroll
+        for (int h = 0; h < kPer; ++h) {
+            if (!((gvalid >> h) & 1u)) continue;
+            const uint4 k = key[h];
+            if (k.x >= lo) atomicAdd(&lds.hist[(k.x - lo) >> sh], 1u);
+            if (k.y >= lo) atomicAdd(&lds.hist[(k.y - lo) >> sh], 1u);
+            if (k.z >= lo) atomicAdd(&lds.hist[(k.z - lo) >> sh], 1u);
+            if (k.w >= lo) atomicAdd(&lds.hist[(k.w - lo) >> sh], 1u);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint32_t order = 0u;
+    if (lane == 0) order = __hip_atomic_fetch_add(&sm.pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    order = __builtin_amdgcn_readfirstlane(order);
+    if (order == 2u) return false;  // the other wave finishes
+    asm volatile("" ::: "memory");
+    uint32_t T = 0u;  // too short to sample, or want out of reach: keep everything
+    bool narrow = false;
+    if (want > 0u) {
+        // lane l holds bins base .. base + 15, base = 1008 - 16 l (the top
+        // bins in lane 0); the want-th key from the top lies in the first
+        // lane whose running sum reaches want, in its bin where the lane's
+        // own running sum, from its top bin down, does
+        const uint32_t base = 1008u - 16u * lane;
+        const uint4* h4 = reinterpret_cast<const uint4*>(lds.hist + base);
+        const uint4 c0 = h4[0], c1 = h4[1], c2 = h4[2], c3 = h4[3];
+        const uint32_t c[16] = {c3.w, c3.z, c3.y, c3.x, c2.w, c2.z, c2.y, c2.x,
+                                c1.w, c1.z, c1.y, c1.x, c0.w, c0.z, c0.y, c0.x};
+        uint32_t own = 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) own += c[j];
+        const uint32_t incl = wave_inclusive_sum(own);
+        const int ol = __ffsll((unsigned long long)__ballot(incl - own < want && want <= incl)) - 1;
+        uint32_t acc = incl - own, digit = 0u;
+        bool hit = false;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const bool here = !hit && acc + c[j] >= want;
+            digit = here ? base + 15u - (uint32_t)j : digit;
+            hit = hit || here;
+            acc += c[j];
+        }
+        digit = (uint32_t)__builtin_amdgcn_readlane((int)digit, ol);
+        T = lo + (digit << sh);
+        narrow = sh > kPairFineShift;
+        // the histogram back to zero for the sampler's next use
+        uint4* z4 = reinterpret_cast<uint4*>(lds.hist + base);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z4[j] = make_uint4(0u, 0u, 0u, 0u);
+        WaveScope::sync();
+    }
+    if (narrow) {
+        // the bin is too wide: the whole search again by this wave
+        sample_select<WaveScope>(sm, R, lds);
+    } else {
+        const uint32_t rest = hi - T;
+        const int wbits = rest == 0u ? 0 : 32 - __clz(rest);
+        if (lane == 0) {
+            R.T = T;
+            R.sh = (uint32_t)(wbits > kDigitBits - 1 ? wbits - (kDigitBits - 1) : 0);
+        }
+    }
+    publish(&sm.n_ready, 1u);
+    return true;
 }
 
 // ----------------------------------------------------------------------------
@@ -1394,8 +1490,8 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         sm.ndeferred = 0u;
         sm.ndirect = 0u;
         sm.nrank = 0u;
-        sm.smax = 0u;
         sm.take_cand = 0u;
+        sm.pair = 0u;
         sm.n_claimed = sm.n_ready = sm.n_finished = 0u;
         sm.last_row = -1;
         sm.abort = 0u;
@@ -1432,6 +1528,15 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
             lens[j] = p.lengths[b < p.batch ? b : p.batch - 1];
         }
     }
+    // Row 0's sample goes out with the lengths, by waves 0 and 1 (which load
+    // no chunks), laid out over the full width n_cols; its runs that lie
+    // inside the row are the sample, unless they are under half of what a
+    // layout over the row's own length would hold (then it is loaded again).
+    const bool maybe_sampled =
+        p.force_path == TOPK_PATH_SAMPLED || (p.force_path == TOPK_PATH_AUTO && p.n_cols > (int64_t)cap);
+    const bool spec = maybe_sampled && (ordered || p.batch <= (int64_t)gridDim.x);
+    const SamplePlan wide(p.n_cols);
+    if (spec && wave_id() < 2) sample_issue_pair(p, sm, b0, wide, wave_id());
     L0 = L0 < 0 ? 0 : (L0 > p.n_cols ? p.n_cols : L0);
 #pragma unroll
     for (int j = 0; j < kLenPer; ++j) {
@@ -1446,12 +1551,16 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
     const bool early = stream0 && (ordered || p.batch <= (int64_t)gridDim.x);
     const bool sampled0 = early && kind0 == kKindSampled;
     const bool queue_later = ordered;  // the table is made by the sampler wave once the roles start
-    SampleRegs<B> sample;
-    if (sampled0) sample.issue(p, b0, L0);
+    const int wide_runs = wide.runs_within(L0);
+    const bool wide_ok = spec && wide_runs >= 2 && 2 * wide_runs >= SamplePlan(L0).runs;
     if (stream0 && threadIdx.x == 0) {
         fill_slot(sm.slot[0], p, b0, L0, kind0);
+        if (wide_ok) sm.slot[0].nsv = (uint32_t)wide_runs * (kRunLen / 4);
         sm.chunk_next[0] = early ? 2u * (uint32_t)kStreamers : 0u;
     }
+    // a sample not used: wave 0's loads land before the sampler wave loads
+    // another into the same LDS (wave 1's own land in order)
+    if (spec && !sampled0 && wave_id() == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);
     if (queue_later) {
         queue_count(p, sm, queue_lds(sm), L0, lens);
         if (threadIdx.x == 0) sm.n_claimed = stream0 ? 1u : 0u;
@@ -1466,7 +1575,6 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
             if (lane_id() == 0) sm.n_claimed = 2u;
         }
     }
-    if (sampled0) sample.store(sm, L0);
     B::sync();
     Chunk a, b;
     Streamer st{p, sm, cap, 0, kNone, -1, -1, 0u, 0u, 0};
@@ -1508,13 +1616,14 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         sample_select<B>(sm, sm.slot[0], sampler_lds);
     }
     if (sampled0) {
-        // row 0's cutoff from the sample by the sampler wave alone, while the
+        // row 0's cutoff from the sample by waves 0 and 1, while the
         // streaming waves issue their chunks' loads (a wave that issues
         // loads waits until the compute unit's memory queue takes them, so
         // a cutoff found by the whole workgroup would wait for the queue)
-        if (wave_id() == 1) {
-            sample_select<WaveScope>(sm, sm.slot[0], sampler_lds);
-            publish(&sm.n_ready, 1u);
+        if (wave_id() < 2) {
+            if (!wide_ok) sample_issue_pair(p, sm, b0, SamplePlan(L0), wave_id());
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            sample_select_pair(sm, sm.slot[0], sampler_lds, wave_id());
         }
     } else {
         // row 0's cutoff is set (or there is no row 0), unless the sampler
@@ -1554,7 +1663,9 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         // known (its loads wait behind the streaming waves' loads); the row
         // claimed from the table is that row unless it is deferred.
         int64_t issued = -1;  // the row whose sample is in flight
-        if (queue_later) {
+        // row 0's sample is read until its cutoff is set
+        const bool alive = !sampled0 || wait_for(sm, &sm.n_ready, 1u);
+        if (alive && queue_later) {
             queue_table(p, sm, queue_lds(sm), [&](int64_t b, int64_t L) {
                 if (row_kind(p, L) != kKindSampled) return;
                 RowSlot R;
@@ -1577,7 +1688,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
                 publish(&sm.n_ready, 1u);
             }
         }
-        for (int j = 1;; ++j) {
+        for (int j = 1; alive; ++j) {
             const int s = j % kSlots;
             if (!sm.slot[s].valid) break;
             if (sm.slot[s].kind == kKindSampled) {

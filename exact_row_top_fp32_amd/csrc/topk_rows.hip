@@ -798,6 +798,7 @@ __device__ __forceinline__ bool sample_select_pair(Shared& sm, RowSlot& R, Selec
     constexpr int kPer = kMaxSample / 4 / 128;  // 4-key groups per lane
     constexpr int kQ = 4;
     constexpr int kPairBits = 10;  // 1024 bins, 16 per lane
+    static_assert((1 << kPairBits) + 64 <= kBins, "room for a sink bin per lane past the bins");
     const int nsv = (int)R.nsv;
     const uint32_t want = sample_want(R);
     const uint32_t lane = lane_id();
@@ -817,14 +818,19 @@ __device__ __forceinline__ bool sample_select_pair(Shared& sm, RowSlot& R, Selec
     }
     const uint32_t q = (want + 127u) / 128u;
     uint32_t top[kQ] = {0u, 0u, 0u, 0u};  // the lane's largest group maxima, descending
+    if (q <= 1u) {  // the lane's maximum is all the bound needs
 #pragma unroll
-    for (int h = 0; h < kPer; ++h) {
-        uint32_t v = max(max(key[h].x, key[h].y), max(key[h].z, key[h].w));  // 0 outside the sample
+        for (int h = 0; h < kPer; ++h) top[0] = max(top[0], max(max(key[h].x, key[h].y), max(key[h].z, key[h].w)));
+    } else {
 #pragma unroll
-        for (int j = 0; j < kQ; ++j) {
-            const uint32_t up = max(top[j], v);
-            v = min(top[j], v);
-            top[j] = up;
+        for (int h = 0; h < kPer; ++h) {
+            uint32_t v = max(max(key[h].x, key[h].y), max(key[h].z, key[h].w));  // 0 outside the sample
+#pragma unroll
+            for (int j = 0; j < kQ; ++j) {
+                const uint32_t up = max(top[j], v);
+                v = min(top[j], v);
+                top[j] = up;
+            }
         }
     }
     uint32_t mine = 0u;
@@ -844,14 +850,18 @@ __device__ __forceinline__ bool sample_select_pair(Shared& sm, RowSlot& R, Selec
     const int wb = span == 0u ? 0 : 32 - __clz(span);
     const int sh = wb > kPairBits ? wb - kPairBits : 0;  // span >> sh < 1024
     if (want > 0u) {
+        // every key counted without a branch: keys below lo, and groups
+        // outside the sample, into a bin of the lane's own past the 1024
+        // (cleared by the wave that finishes)
+        const uint32_t sink = 1024u + lane;
 #pragma unroll
         for (int h = 0; h < kPer; ++h) {
-            if (!((gvalid >> h) & 1u)) continue;
+            const bool in = (gvalid >> h) & 1u;
             const uint4 k = key[h];
-            if (k.x >= lo) atomicAdd(&lds.hist[(k.x - lo) >> sh], 1u);
-            if (k.y >= lo) atomicAdd(&lds.hist[(k.y - lo) >> sh], 1u);
-            if (k.z >= lo) atomicAdd(&lds.hist[(k.z - lo) >> sh], 1u);
-            if (k.w >= lo) atomicAdd(&lds.hist[(k.w - lo) >> sh], 1u);
+            atomicAdd(&lds.hist[in && k.x >= lo ? (k.x - lo) >> sh : sink], 1u);
+            atomicAdd(&lds.hist[in && k.y >= lo ? (k.y - lo) >> sh : sink], 1u);
+            atomicAdd(&lds.hist[in && k.z >= lo ? (k.z - lo) >> sh : sink], 1u);
+            atomicAdd(&lds.hist[in && k.w >= lo ? (k.w - lo) >> sh : sink], 1u);
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -893,6 +903,7 @@ __device__ __forceinline__ bool sample_select_pair(Shared& sm, RowSlot& R, Selec
         uint4* z4 = reinterpret_cast<uint4*>(lds.hist + base);
 #pragma unroll
         for (int j = 0; j < 4; ++j) z4[j] = make_uint4(0u, 0u, 0u, 0u);
+        lds.hist[1024u + lane] = 0u;
         WaveScope::sync();
     }
     if (narrow) {
@@ -1663,6 +1674,9 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
         // known (its loads wait behind the streaming waves' loads); the row
         // claimed from the table is that row unless it is deferred.
         int64_t issued = -1;  // the row whose sample is in flight
+        // ahead of the streaming waves on its SIMD: the next cutoff is due
+        // before the current row is streamed
+        __builtin_amdgcn_s_setprio(3);
         // row 0's sample is read until its cutoff is set
         const bool alive = !sampled0 || wait_for(sm, &sm.n_ready, 1u);
         if (alive && queue_later) {
@@ -1704,7 +1718,12 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
             claim_row(p, sm, sm.slot[sn], sampler_lds, &sm.semitted);
             publish(&sm.n_claimed, (uint32_t)j + 2u);
         }
+        __builtin_amdgcn_s_setprio(0);
     } else {
+        // streaming waves ahead of the finisher on their SIMD: its long
+        // dependent chains otherwise take issue cycles from the two
+        // streaming waves beside it
+        __builtin_amdgcn_s_setprio(2);
         bool more = st.c < kNone;  // a chunk of row 0 or 1 issued at the start
         if (!more && st.c != kEnd) {
             st.c = st.grab(st.i, INT32_MAX, false);
@@ -1715,6 +1734,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(Params p) {
             more = st.step(a, b);
             if (more) more = st.step(b, a);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     B::sync();
     if (sm.abort != 0u && threadIdx.x == 0) atomicAdd(&g_watchdog_trips, 1u);

@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "exact_topk.h"
 #include "topk_device.h"
@@ -87,7 +88,24 @@ struct SplitParams {
     uint2* surv;         // [batch][kSplitCapacity]: (raw score bits, position)
     int64_t piece_vec;   // 4-score groups per piece, a multiple of kRound
     int32_t pieces;      // workgroups per row
+    uint32_t page_magic;  // position / page_size = (position * page_magic) >> page_shift
+    int32_t page_shift;
 };
+
+// Division by the page size as a multiply, exact for positions below 2^31
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994: with l = ceil(log2 d), the 32-bit multiplier
+// ceil(2^(31 + l) / d) and a shift by 31 + l).
+inline void page_divider(int32_t page_size, uint32_t& magic, int32_t& shift) {
+    magic = 0u;
+    shift = 0;
+    if (page_size < 1) return;
+    const uint64_t d = (uint64_t)page_size;
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    magic = (uint32_t)(((1ull << (31 + l)) + d - 1) / d);
+    shift = 31 + l;
+}
 
 constexpr int64_t kSplitCapacity = 8192;  // survivor entries per row in the workspace
 
@@ -113,13 +131,49 @@ __device__ __forceinline__ void split_stats(const SplitParams& p, int64_t b, int
     }
 }
 
-// Keys held in an LDS array, position = array index.
-struct LdsKeys {
-    const uint32_t* key;
-    uint32_t n;
+// A lane's sample keys held in registers: kLoads loads of kPer keys each,
+// load h present when h * kThreads + threadIdx.x < nload (the workgroup's
+// loads). The views of the sample ignore positions.
+template <int kLoads, int kPer>
+struct RegKeys {
+    const uint32_t (&key)[kLoads * kPer];
+    int nload;
     template <class F>
-    __device__ void for_each(F&& f) const {
-        for (uint32_t e = threadIdx.x; e < n; e += kThreads) f(key[e], e);
+    __device__ void for_each_slot(F&& f) const {
+#pragma unroll
+        for (int h = 0; h < kLoads; ++h) {
+            const bool valid = h * kThreads + (int)threadIdx.x < nload;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) f(key[h * kPer + j], 0u, valid);
+        }
+    }
+};
+
+// Survivors held in registers, N slots per lane: slot i of a lane holds the
+// raw score bits and the position of one survivor, or all-ones bits and the
+// position 0xFFFFFFFF (no survivor; positions are below 2^31). Slots at or
+// past `nslot` are empty on every lane. Slots are visited in groups of
+// kGroup, a group wholly past nslot skipped by one uniform test (a test per
+// slot would hold a mask register per slot).
+constexpr int kGroup = 4;
+template <int N>
+struct RegPairs {
+    uint32_t bits[N];
+    uint32_t idx[N];
+    int nslot;
+    template <class F>
+    __device__ __forceinline__ void for_each_group(F&& f) const {
+#pragma unroll
+        for (int g = 0; g < N; g += kGroup) {
+            if (g < nslot) {
+#pragma unroll
+                for (int i = g; i < (g + kGroup < N ? g + kGroup : N); ++i) f(i);
+            }
+        }
+    }
+    template <class F>
+    __device__ __forceinline__ void for_each_slot(F&& f) const {
+        for_each_group([&](int i) { f(order_key(__uint_as_float(bits[i])), idx[i], idx[i] != 0xFFFFFFFFu); });
     }
 };
 
@@ -127,12 +181,73 @@ struct LdsKeys {
 // score rows and their sampled cutoff (both the split-row and short-row kernels)
 // ----------------------------------------------------------------------------
 
+// The least sh with (d >> sh) <= kBins - 3, so that a span of d + 1 keys
+// fits kBins - 2 bins of width 2^sh: the top bit of d placed at bit 10, one
+// more when that still leaves d >> sh at kBins - 2 or above.
+__device__ __forceinline__ int bin_shift(uint32_t d) {
+    const int top = 31 - (int)__clz(d | 1u);
+    const int sh0 = top > kDigitBits - 1 ? top - (kDigitBits - 1) : 0;
+    return sh0 + ((d >> sh0) >= (uint32_t)(kBins - 2) ? 1 : 0);
+}
+
+// Radix selection as radix_select does it, over a source that yields every
+// register slot, valid or not (Src::for_each_slot): the histogram updates
+// take no branches, a slot outside the pass adding to its lane's sink bin
+// hist[kBins + lane], which nothing reads. hist holds kBins + 64 words.
+template <class S, class Src, class View>
+__device__ __forceinline__ Cut radix_select_slots(SelectLds lds, const Src& src, View view, uint32_t rank,
+                                                  uint32_t prefix, int nbits, uint32_t equal_if_none) {
+    Cut cut{prefix, rank, equal_if_none, false};
+    const uint32_t sink = (uint32_t)kBins + lane_id();
+    while (nbits > 0) {
+        const int w = nbits < kDigitBits ? nbits : kDigitBits;
+        const int shift = nbits - w;
+        const uint32_t done_mask = nbits >= 32 ? 0u : (0xFFFFFFFFu << nbits);
+        const uint32_t want = prefix & done_mask;
+        const uint32_t dmask = (1u << w) - 1u;
+        src.for_each_slot([&](uint32_t key, uint32_t idx, bool valid) {
+            uint32_t v;
+            const bool in = view(key, idx, v) && valid && (v & done_mask) == want;
+            atomicAdd(&lds.hist[in ? (v >> shift) & dmask : sink], 1u);
+        });
+        S::sync();
+        const Found f = find_rank_bin<S>(lds, rank);
+        rank -= f.above;
+        prefix = want | (f.digit << shift);
+        nbits = shift;
+        cut.equal = f.count;
+        if (nbits > 0 && f.count == rank) {
+            cut.value = prefix;
+            cut.range = true;
+            return cut;
+        }
+    }
+    cut.value = prefix;
+    cut.need = rank;
+    return cut;
+}
+
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 // Element types of a score row, read 16 bytes at a time: fp32, or bf16 (its
 // bit pattern, the top half of the fp32 it denotes exactly). bits() gives the
 // fp32 pattern of element j of a load, so keys, survivors and selection are
 // the fp32 ones for both.
+//
+// pass<kPos>() is the survivor test key >= T on a load's raw bits, one integer
+// compare per score, exact for every non-NaN score (SurvivorBound holds the
+// bounds): with T at or above the key of +0 (kPos), a score passes when its
+// bits as a signed integer reach T ^ 0x80000000, and below it when its bits as
+// an unsigned integer are at most ~T. A load of all-ones words (a NaN
+// pattern) fails both tests once T is at least kMinT: lanes past a row's end
+// load it instead (g_pad).
+struct SurvivorBound {
+    uint32_t t;   // kPos: T ^ 0x80000000 (signed compare); else ~T (unsigned)
+    uint32_t th;  // bf16: the same bound for a score's 16 bits, compared in place in its half word
+};
+constexpr uint32_t kMinT = 0x10000u;  // below -inf's key 0x007FFFFF: every non-NaN score passes
+__device__ __align__(16) const uint32_t g_pad[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+
 struct F32Elem {
     typedef f4 Vec;
     typedef float Scalar;
@@ -142,6 +257,16 @@ struct F32Elem {
     __device__ static uint32_t scalar_bits(Scalar x) { return __float_as_uint(x); }
     static constexpr int kKeyShift = 0;  // every key bit carries information
     __device__ static uint32_t full_key(uint32_t v) { return v; }
+    __device__ static SurvivorBound bound(uint32_t T, bool pos) {
+        const uint32_t t = pos ? (T ^ 0x80000000u) : ~T;
+        return SurvivorBound{t, t};
+    }
+    template <bool kPos>
+    __device__ static bool pass(const Vec& v, int j, SurvivorBound b, uint32_t& out_bits) {
+        const uint32_t x = __float_as_uint(v[j]);
+        out_bits = x;
+        return kPos ? (int32_t)x >= (int32_t)b.t : x <= b.t;
+    }
 };
 struct Bf16Elem {
     typedef u4 Vec;
@@ -157,6 +282,25 @@ struct Bf16Elem {
     // a negative one, so selecting on key >> 16 is exact.
     static constexpr int kKeyShift = 16;
     __device__ static uint32_t full_key(uint32_t v) { return (v << 16) | ((v >> 15) & 1u ? 0u : 0xFFFFu); }
+    // A score is tested on its 16 bits in place: its widened bits h << 16,
+    // as a signed integer, reach t >= 0 exactly when h as a signed 16-bit
+    // integer reaches ceil(t / 2^16); as an unsigned integer they stay at or
+    // below t exactly when h stays at or below floor(t / 2^16).
+    __device__ static SurvivorBound bound(uint32_t T, bool pos) {
+        if (pos) {
+            const uint32_t t = T ^ 0x80000000u;  // at most 0x7FFFFFFF
+            return SurvivorBound{t, (uint32_t)(((uint64_t)t + 0xFFFFu) >> 16)};  // at most 2^15
+        }
+        const uint32_t t = ~T;
+        return SurvivorBound{t, t >> 16};
+    }
+    template <bool kPos>
+    __device__ static bool pass(const Vec& v, int j, SurvivorBound b, uint32_t& out_bits) {
+        const uint32_t w = v[j >> 1];
+        const uint32_t h = (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+        out_bits = (j & 1) ? (w & 0xFFFF0000u) : (w << 16);
+        return kPos ? (int32_t)(int16_t)h >= (int32_t)b.th : h <= b.th;
+    }
 };
 
 template <class E>
@@ -232,8 +376,8 @@ struct Cutoff {
 };
 
 template <class E, class Issue = NoIssue>
-__device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, uint32_t* skey,
-                               SelectLds lds, Issue&& issue = Issue{}) {
+__device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, SelectLds lds,
+                               Issue&& issue = Issue{}) {
     using B = BlockScope<kThreads>;
     const int64_t fit = L / (2 * kRunLen);
     const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
@@ -267,14 +411,17 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
     constexpr int kQ = 4;
     uint32_t top[kQ] = {0u, 0u, 0u, 0u};
     uint32_t fin = 0u;  // the lane's largest key below +inf's
+    uint32_t skey[kPer * E::kPerVec];
+    const RegKeys<kPer, E::kPerVec> keys{skey, nsv};
 #pragma unroll
     for (int h = 0; h < kPer; ++h) {
         const int t = h * kThreads + (int)threadIdx.x;
+#pragma unroll
+        for (int j = 0; j < E::kPerVec; ++j) skey[h * E::kPerVec + j] = elem_key<E>(E::bits(x[h], j));
         if (t < nsv) {
 #pragma unroll
             for (int j = 0; j < E::kPerVec; ++j) {
-                uint32_t key = elem_key<E>(E::bits(x[h], j));
-                skey[E::kPerVec * t + j] = key;
+                uint32_t key = skey[h * E::kPerVec + j];
                 fin = max(fin, key < kInfKey ? key : 0u);
 #pragma unroll
                 for (int i = 0; i < kQ; ++i) {
@@ -287,6 +434,11 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
     }
     const uint32_t q = (want + kThreads - 1) / kThreads;
     const bool one_pass = want > 0u && q <= (uint32_t)kQ;  // uniform
+    // With q <= kQ the histograms take only each lane's kQ largest keys (0
+    // for a lane with fewer): a subset of the sample, so its want-th largest
+    // key is at or below the sample's and T stays a valid cutoff; it is
+    // lower only by the keys of lanes holding more than kQ above it.
+    const RegKeys<1, kQ> cand{top, kThreads};
     __shared__ uint32_t s_lo, s_hi;
     if (threadIdx.x == 0) {
         s_lo = 0xFFFFFFFFu;
@@ -311,10 +463,9 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
         // the want-th largest key, or hi + 1 when that key is above hi (bf16
         // keys differ by at least 2^16, so their bins hold one value each)
         const uint32_t lo = s_lo, hi = max(shi, lo);
-        int sh = 0;
-        while (((hi - lo) >> sh) >= (uint32_t)(kBins - 2)) ++sh;
+        const int sh = bin_shift(hi - lo);
         const uint32_t base = lo & ~((1u << sh) - 1u);  // (hi - base) >> sh <= kBins - 2
-        const Cut c = radix_select<B>(lds, LdsKeys{skey, n}, SampleBinView{lo, hi, base, sh}, want, 0u, kDigitBits, n);
+        const Cut c = radix_select_slots<B>(lds, cand, SampleBinView{lo, hi, base, sh}, want, 0u, kDigitBits, n);
         if (c.value == (uint32_t)(kBins - 1)) return Cutoff{hi + 1u, shi};
         const uint32_t edge = base + (c.value << sh);
         // A few far keys (peaks well above a dense bulk) stretch [lo, hi] so
@@ -325,8 +476,8 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
         // bin alone, 2^10 times finer, places T.
         if (sh > 0 && 4u * (c.equal - c.need) > want) {
             const int sh2 = sh > kDigitBits - 1 ? sh - (kDigitBits - 1) : 0;
-            const uint32_t top = min(edge + ((1u << sh) - 1u), hi);  // no overflow: hi < +inf's key
-            const Cut c2 = radix_select<B>(lds, LdsKeys{skey, n}, SubBinView{edge, max(edge, lo), top, sh2},
+            const uint32_t bin_top = min(edge + ((1u << sh) - 1u), hi);  // no overflow: hi < +inf's key
+            const Cut c2 = radix_select_slots<B>(lds, cand, SubBinView{edge, max(edge, lo), bin_top, sh2},
                                            c.need, 0u, kDigitBits, c.equal);
             return Cutoff{edge + (c2.value << sh2), shi};
         }
@@ -334,7 +485,7 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
     }
     constexpr int kDropBits = 32 - 2 * kDigitBits;
     const uint32_t T =
-        radix_select<B>(lds, LdsKeys{skey, n}, CoarseKeyView<kDropBits>{}, want, 0u, 2 * kDigitBits, n).value
+        radix_select_slots<B>(lds, keys, CoarseKeyView<kDropBits>{}, want, 0u, 2 * kDigitBits, n).value
         << kDropBits;
     return Cutoff{T, shi};
 }
@@ -345,8 +496,7 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
 
 __global__ __launch_bounds__(kThreads) void split_sample_kernel(SplitParams p) {
     using B = BlockScope<kThreads>;
-    __shared__ uint32_t skey[kMaxSample];
-    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t hist[kBins + 64];
     __shared__ uint32_t found[3];
     for (int i = (int)threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
     B::sync();
@@ -367,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void split_sample_kernel(SplitParams p) {
         kind = kKindAll;
     } else {
         kind = kKindSampled;
-        T = short_cutoff<F32Elem>(p.scores + b * p.row_stride, L, m, skey, SelectLds{hist, found}).T;
+        T = short_cutoff<F32Elem>(p.scores + b * p.row_stride, L, m, SelectLds{hist, found}).T;
     }
     if (threadIdx.x == 0) p.head[b] = SplitHead{0u, 0u, T, kind};
 }
@@ -474,6 +624,17 @@ struct ShiftedRangeView {
     }
 };
 
+// A selection among survivors: keys above kth are taken; keys equal to kth
+// are taken when their position is at most icut, or, with need > 0, the
+// need lowest positions of the `equal` (at most 64) tied survivors are.
+struct SurvSel {
+    uint32_t kth;
+    int32_t icut;
+    uint32_t need;
+    uint32_t equal;
+    __device__ static SurvSel of(Selection s) { return SurvSel{s.kth, s.icut, 0u, 0u}; }
+};
+
 // Exact top m of a row's survivors held in LDS by workgroup scope B (keys at
 // least T; the short-row and split-finish kernels), ties at the cutoff to the
 // lowest positions, as select_top does, with three savings. Keys are
@@ -484,80 +645,196 @@ struct ShiftedRangeView {
 // their top 11 bits share (bins of width 1 settle the cutoff in that pass);
 // hi need not bound every survivor (the sample's largest finite key serves),
 // and +inf does not stretch the bins. And when at most 64 survivors equal
-// the cutoff key, their positions are gathered and ranked by one wave
-// instead of by radix passes over the positions. `ties` is 66 words of LDS,
-// ties[64] zero on entry.
-template <class E, class B>
-__device__ Selection short_select(SelectLds lds, const PairSource<B>& src, uint32_t m, uint32_t n, uint32_t T,
-                                  uint32_t hi_key, int idx_bits, uint32_t* ties) {
+// the cutoff key and only some of them are taken, the emission ranks their
+// positions (SurvSel::need) instead of radix passes over the positions.
+template <class E, class B, class Src>
+__device__ SurvSel short_select(SelectLds lds, const Src& src, uint32_t m, uint32_t n, uint32_t T, uint32_t hi_key,
+                                int idx_bits) {
     constexpr int kShift = E::kKeyShift;
     constexpr uint32_t kTop = 0xFFFFFFFFu >> kShift;
     const uint32_t lo = T >> kShift, hi = max(hi_key >> kShift, lo);
-    int sh = 0;
-    while (((hi - lo) >> sh) >= (uint32_t)(kBins - 2)) ++sh;
+    const int sh = bin_shift(hi - lo);
     const uint32_t base = lo & ~((1u << sh) - 1u);  // (hi - base) >> sh <= kBins - 2
-    const Cut c1 = radix_select<B>(lds, src, AboveBinView<kShift>{base, hi, sh}, m, 0u, kDigitBits, n);
+    const Cut c1 = radix_select_slots<B>(lds, src, AboveBinView<kShift>{base, hi, sh}, m, 0u, kDigitBits, n);
     Cut c;
     if (c1.value == (uint32_t)(kBins - 1)) {  // the cutoff is above hi (so hi < kTop)
-        if (c1.need == c1.equal) return at_least((hi + 1u) << kShift);
-        c = radix_select<B>(lds, src, ShiftedRangeView<kShift>{hi + 1u, kTop}, c1.need, 0u, 32 - kShift, c1.equal);
-        if (c.range) return at_least(c.value << kShift);
+        if (c1.need == c1.equal) return SurvSel::of(at_least((hi + 1u) << kShift));
+        c = radix_select_slots<B>(lds, src, ShiftedRangeView<kShift>{hi + 1u, kTop}, c1.need, 0u, 32 - kShift,
+                                  c1.equal);
+        if (c.range) return SurvSel::of(at_least(c.value << kShift));
     } else {
         const uint32_t edge = base + (c1.value << sh);  // lowest value in the cutoff bin
-        if (c1.need == c1.equal) return at_least(edge << kShift);  // the bin is taken whole
+        if (c1.need == c1.equal) return SurvSel::of(at_least(edge << kShift));  // the bin is taken whole
         c = Cut{edge, c1.need, c1.equal, false};
         if (sh > 0) {
             // the bin's keys share the bits above sh; keys above hi with
             // those bits were counted in the top bin, so they stay out
-            c = radix_select<B>(lds, src, ShiftedRangeView<kShift>{edge, hi}, c1.need, edge, sh, c1.equal);
-            if (c.range) return at_least(c.value << kShift);  // the least full key whose top bits reach c.value
+            c = radix_select_slots<B>(lds, src, ShiftedRangeView<kShift>{edge, hi}, c1.need, edge, sh, c1.equal);
+            if (c.range) return SurvSel::of(at_least(c.value << kShift));  // the least full key whose top bits reach c.value
         }
     }
     const uint32_t kth = E::full_key(c.value);
-    Selection sel{kth, INT32_MAX};
-    if (c.need >= c.equal) return sel;
-    if (c.equal <= 64u) {
-        // exactly c.equal survivors have the cutoff key
-        src.for_each([&](uint32_t key, uint32_t idx) {
-            if (key == kth) ties[atomicAdd(&ties[64], 1u)] = idx;
-        });
-        B::sync();
-        if (B::first_wave()) {
-            // positions are distinct: the lane whose position has need - 1
-            // smaller ones holds the cutoff position
-            const uint32_t lane = lane_id();
-            const uint32_t v = lane < c.equal ? ties[lane] : 0xFFFFFFFFu;
-            uint32_t below = 0u;
-            for (uint32_t j = 0; j < c.equal; ++j) below += __shfl(v, (int)j) < v ? 1u : 0u;
-            if (lane < c.equal && below == c.need - 1u) ties[65] = v;
-        }
-        B::sync();
-        sel.icut = (int32_t)ties[65];
-        return sel;
-    }
+    if (c.need >= c.equal) return SurvSel{kth, INT32_MAX, 0u, 0u};
+    if (c.equal <= (uint32_t)kMaxCand) return SurvSel{kth, 0, c.need, c.equal};  // ranked by the emission
     // the need-th largest inverted index among the ties (select_top's way)
     const uint32_t iprefix = idx_bits >= 32 ? 0u : (0xFFFFFFFFu << idx_bits);
-    const Cut t = radix_select<B>(lds, src, TieIndexView{kth}, c.need, iprefix, idx_bits, c.equal);
-    sel.icut = (int32_t)(~t.value);
-    return sel;
+    const Cut t = radix_select_slots<B>(lds, src, TieIndexView{kth}, c.need, iprefix, idx_bits, c.equal);
+    return SurvSel{kth, (int32_t)(~t.value), 0u, 0u};
+}
+
+// Positions to output values: the identity, or the page-table transform
+// page_table[b, i / page_size] * page_size + i % page_size (truncated to
+// int32 as the 64-bit value would be), with the row's entries staged in LDS
+// for a power-of-two page size, else read from global memory with the
+// division done by a multiply. Each takes any position a caller passes
+// (the emission clamps unused lanes to 0 first).
+struct NoMap {
+    __device__ __forceinline__ int32_t operator()(uint32_t i) const { return (int32_t)i; }
+};
+typedef __attribute__((address_space(1))) const int32_t* GlobalI32;
+typedef __attribute__((address_space(3))) const int32_t* LdsI32;
+struct LdsShiftMap {
+    LdsI32 pages;  // the row's entries, staged in LDS
+    uint32_t l;    // page_size = 2^l
+    __device__ __forceinline__ int32_t operator()(uint32_t i) const {
+        return (int32_t)(((uint32_t)pages[i >> l] << l) | (i & ((1u << l) - 1u)));
+    }
+};
+struct GlobalMagicMap {
+    GlobalI32 pages;  // the row's entries in global memory
+    uint32_t d, magic;
+    int shift;
+    __device__ __forceinline__ int32_t operator()(uint32_t i) const {
+        const uint32_t q = (uint32_t)(((uint64_t)i * magic) >> shift);
+        return (int32_t)((uint32_t)pages[q] * d + (i - q * d));
+    }
+};
+
+__device__ __forceinline__ GlobalMagicMap global_map(const SplitParams& p, int64_t b) {
+    return GlobalMagicMap{(GlobalI32)(p.page_table + b * p.pt_stride), (uint32_t)p.page_size, p.page_magic,
+                          p.page_shift};
+}
+
+// LDS words the emission works in: the output list (m <= TOPK_MAX_K entries,
+// then one spare word per lane), then each wave's 64-word tie region, then
+// one spare word per lane for the ties.
+constexpr int kListWords = TOPK_MAX_K + 64;
+template <int kWaves>
+constexpr int emit_words() { return kListWords + 64 * kWaves + 64; }
+
+// Writes the survivors a SurvSel takes, from the registers that hold them.
+// Each lane counts the entries it takes; a wave prefix sum and the waves'
+// totals give every lane its run of places in an LDS list, where the lanes
+// write their entries already mapped (an entry not taken goes to the lane's
+// spare word, so no write branches); after a barrier the list is copied to
+// the output row, coalesced. Ranked ties (SurvSel::need > 0): each lane
+// writes its tied positions to its wave's 64-word tie region in the same
+// way, and one wave finds the need-th smallest of the `equal` (<= 64) of
+// them, bit by bit from the top of idx_bits, and lists the need lowest after
+// the rest. The work is vector instructions with few scalar round trips, so
+// that a lone wave per SIMD is not held up between them. wtot holds two
+// words per wave; ws emit_words<kWaves>() words. A selection holds exactly m
+// entries; the bounds only keep a defect from writing outside the row or
+// the LDS areas.
+template <class B, int N, class Map>
+__device__ __forceinline__ void emit_slots(const RegPairs<N>& sv, SurvSel sel, uint32_t m, int32_t* row,
+                                           const Map& map, int idx_bits, uint32_t* wtot, uint32_t* ws) {
+    constexpr int kWaves = B::kSize / 64;
+    const uint32_t w = wave_id(), lane = lane_id();
+    uint32_t* lst = ws;
+    uint32_t* tw = ws + kListWords;
+    // an empty slot holds all-ones bits, key 0, below every cutoff key (at
+    // least kMinT), so it is neither taken nor tied
+    const bool by_icut = sel.need == 0u;
+    auto look = [&](int i, bool& tie) {
+        const uint32_t key = order_key(__uint_as_float(sv.bits[i]));
+        tie = (key == sel.kth) & !by_icut;
+        return (key > sel.kth) | ((key == sel.kth) & by_icut & ((int32_t)sv.idx[i] <= sel.icut));
+    };
+    uint32_t cnt = 0u, tcnt = 0u;
+    sv.for_each_group([&](int i) {
+        bool tie;
+        cnt += look(i, tie) ? 1u : 0u;
+        tcnt += tie ? 1u : 0u;
+    });
+    const uint32_t incl = wave_inclusive_sum(cnt);
+    uint32_t tpos = 64u * w;
+    if (!by_icut) {
+        const uint32_t tincl = wave_inclusive_sum(tcnt);
+        tpos += tincl - tcnt;
+        if (lane == 63u) wtot[kWaves + w] = tincl;
+        const uint32_t tspare = (uint32_t)(64 * kWaves) + lane;
+        const uint32_t tend = 64u * w + 64u;
+        sv.for_each_group([&](int i) {
+            bool tie;
+            look(i, tie);
+            tw[(tie & (tpos < tend)) ? tpos : tspare] = sv.idx[i];
+            tpos += tie ? 1u : 0u;
+        });
+    }
+    if (lane == 63u) wtot[w] = incl;
+    B::sync();
+    uint32_t base = incl - cnt, total = 0u;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const uint32_t c = wtot[i];
+        base += (uint32_t)i < w ? c : 0u;
+        total += c;
+    }
+    const uint32_t spare = (uint32_t)TOPK_MAX_K + lane;
+    sv.for_each_group([&](int i) {
+        bool tie;
+        const bool t = look(i, tie);
+        const int32_t o = map(t ? sv.idx[i] : 0u);
+        lst[(t & (base < m)) ? base : spare] = (uint32_t)o;
+        base += t ? 1u : 0u;
+    });
+    if (!by_icut && w == 0u) {
+        // lane l takes the l-th gathered tie, wave region by wave region
+        uint32_t v = 0xFFFFFFFFu, first = 0u;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            const uint32_t c = min(wtot[kWaves + i], 64u);
+            if (lane >= first && lane < first + c) v = tw[i * 64 + (lane - first)];
+            first += c;
+        }
+        uint32_t V = 0u;
+        for (int bit = idx_bits - 1; bit >= 0; --bit) {
+            const uint32_t c = V | (1u << bit);
+            if ((uint32_t)__popcll(__ballot(v < c)) < sel.need) V = c;
+        }
+        const bool chosen = v <= V;  // positions are below 2^idx_bits, so the unused lanes stay out
+        const uint32_t slot = total + lanes_below(__ballot(chosen));
+        const int32_t o = map(chosen ? v : 0u);
+        lst[(chosen & (slot < m)) ? slot : spare] = (uint32_t)o;
+    }
+    B::sync();
+    constexpr int kPer = (TOPK_MAX_K + B::kSize - 1) / B::kSize;  // list words per thread, all read at once
+    uint32_t o[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) o[i] = lst[(uint32_t)(i * B::kSize) + threadIdx.x];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const uint32_t j = (uint32_t)(i * B::kSize) + threadIdx.x;
+        if (j < m) row[j] = (int32_t)o[i];
+    }
 }
 
 // launch 3: the exact top m of each row
 __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p) {
     using B = BlockScope<kFinThreads>;
-    __shared__ uint2 lsurv[kSplitCapacity];
-    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t ews[emit_words<kFinThreads / 64>()];  // the emission's list and tie regions
+    __shared__ uint32_t hist[kBins + 64];
     __shared__ uint32_t found[3];
     __shared__ uint32_t emitted;
-    __shared__ uint32_t ties[66];  // tied positions, their count, the cutoff position
-    __shared__ uint32_t smax;      // the largest survivor key
+    __shared__ uint32_t wtot[2 * (kFinThreads / 64)];
+    __shared__ uint32_t smax;  // the largest survivor key
     const int64_t b = blockIdx.x;
     const SplitHead head = p.head[b];
     if (head.kind == kKindDirect) return;
     for (int i = (int)threadIdx.x; i < kBins; i += kFinThreads) hist[i] = 0u;
     if (threadIdx.x == 0) {
         emitted = 0u;
-        ties[64] = 0u;
         smax = 0u;
     }
     const int64_t L = split_row_len(p, b);
@@ -575,34 +852,30 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
         emit(src, s, out);
     } else {
         code = head.kind == kKindAll ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
-        // survivors in 16-byte pairs; an odd count reads one unused entry
-        // past it, still inside the row's area (n < capacity <= area)
-        constexpr int kPer = (int)(kSplitCapacity / 2 / kFinThreads);
-        const uint4* g4 = reinterpret_cast<const uint4*>(p.surv + b * kSplitCapacity);
-        uint4* l4 = reinterpret_cast<uint4*>(lsurv);
-        const uint32_t npair = (n + 1u) / 2u;
-        uint4 v[kPer];
+        // survivors straight into registers, all loads in flight at once
+        constexpr int kSlots = (int)(kSplitCapacity / kFinThreads);
+        const uint2* g = p.surv + b * kSplitCapacity;
+        RegPairs<kSlots> sv;
+        sv.nslot = (int)((n + kFinThreads - 1) / kFinThreads);
 #pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const uint32_t i = (uint32_t)(q * kFinThreads) + threadIdx.x;
-            v[q] = i < npair ? g4[i] : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < kSlots; ++i) {
+            const uint32_t e = (uint32_t)(i * kFinThreads) + threadIdx.x;
+            uint2 v = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+            if (e < n) v = g[e];
+            sv.bits[i] = v.x;
+            sv.idx[i] = v.y;
         }
         uint32_t hmax = 0u;
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-            const uint32_t i = (uint32_t)(q * kFinThreads) + threadIdx.x;
-            if (i < npair) {
-                l4[i] = v[q];
-                hmax = max(hmax, order_key(__uint_as_float(v[q].x)));
-                if (2u * i + 1u < n) hmax = max(hmax, order_key(__uint_as_float(v[q].z)));
-            }
-        }
+        sv.for_each_slot([&](uint32_t key, uint32_t, bool valid) { hmax = max(hmax, valid ? key : 0u); });
         hmax = wave_max(hmax);
         if (lane_id() == 0) atomicMax(&smax, hmax);
         B::sync();
-        const PairSource<B> src{lsurv, n};
-        const Selection s = short_select<F32Elem, B>(lds, src, m, n, head.T, smax, bits_for(L), ties);
-        emit(src, s, out);
+        const SurvSel s = short_select<F32Elem, B>(lds, sv, m, n, head.T, smax, bits_for(L));
+        int32_t* row = p.out + b * (int64_t)p.k;
+        if (p.page_table == nullptr)
+            emit_slots<B>(sv, s, m, row, NoMap{}, bits_for(L), wtot, ews);
+        else
+            emit_slots<B>(sv, s, m, row, global_map(p, b), bits_for(L), wtot, ews);
     }
     if (threadIdx.x == 0) split_stats(p, b, code, head.kind == kKindFull ? (uint32_t)L : n);
 }
@@ -623,13 +896,14 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     constexpr int64_t kR = (int64_t)kThreads * kU;  // loads per workgroup round
     using B = BlockScope<kThreads>;
     typedef typename E::Vec Vec;
-    __shared__ uint2 buf[kShortCap];  // the sample's keys first, then the survivors
-    __shared__ uint32_t hist[kBins];
+    // the survivors (one spare entry per lane past them), later the waves'
+    // tie regions
+    __shared__ uint2 buf[kShortCap + 64];
+    __shared__ uint32_t hist[kBins + 64];
     __shared__ uint32_t found[3];
     __shared__ uint32_t count;
     __shared__ uint32_t emitted;
-    __shared__ uint32_t ties[66];  // tied positions, their count, the cutoff position
-    static_assert(kShortCap * 2 >= kMaxSample, "the sample fits the survivor buffer");
+    __shared__ uint32_t wtot[2 * (kThreads / 64)];
     const int64_t b = blockIdx.x;
     const int64_t L = split_row_len(p, b);
     const uint32_t m = (uint32_t)(L < p.k ? L : p.k);
@@ -643,7 +917,6 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     if (threadIdx.x == 0) {
         count = 0u;
         emitted = 0u;
-        ties[64] = 0u;
     }
     B::sync();
     const SelectLds lds{hist, found};
@@ -665,82 +938,109 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     // sampled row's first two rounds are issued right behind the sample's
     // loads, so that they land while the cutoff is found.
     const int64_t nvec = L / E::kPerVec;
-    const Vec* rv = reinterpret_cast<const Vec*>(row);
+    // global-address-space pointers, so that the loads stay global loads
+    typedef __attribute__((address_space(1))) const Vec* GVec;
+    const GVec rv = (GVec)(reinterpret_cast<const Vec*>(row));
+    const GVec pad = (GVec)(reinterpret_cast<const Vec*>(g_pad));
+    // Every lane loads: a lane past the row's full loads reads the padding,
+    // which no score test passes, so the filter needs no bounds. With a fixed
+    // number of loads issued after the sample's, the sample can be used once
+    // its own loads are in, these still in flight.
     auto load = [&](int64_t base, Vec (&x)[kU]) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t g = base + u * kThreads + threadIdx.x;
-            if (g < nvec) x[u] = __builtin_nontemporal_load(rv + g);
+            x[u] = __builtin_nontemporal_load(g < nvec ? rv + g : pad);
         }
     };
     Vec xa[kU], xc[kU];
-    // Every lane loads; a lane past the row's full loads takes the last one
-    // again (the filter skips it). With a fixed number of loads issued after
-    // the sample's, the sample can be used once its own loads are in, these
-    // still in flight. A row with a sample has at least 2 * kRunLen * 2
-    // scores, so nvec >= 1 there; a row too short to sample (only when the
-    // sampled path is forced) may have no full load at all and then loads
-    // nothing.
-    auto first_loads = [&](bool sampled) {
-        if (!sampled && nvec == 0) return;
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int64_t g = u * kThreads + threadIdx.x;
-            xa[u] = __builtin_nontemporal_load(rv + (g < nvec ? g : nvec - 1));
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int64_t g = kR + u * kThreads + threadIdx.x;
-            xc[u] = __builtin_nontemporal_load(rv + (g < nvec ? g : nvec - 1));
-        }
+    // the scores past the last full load, [tail0, L): one per lane of the
+    // first wave, loaded with the first rounds (all ones, a NaN pattern that
+    // fails the survivor test, on the other lanes)
+    const int64_t tail0 = nvec * E::kPerVec;
+    typedef __attribute__((address_space(1))) const typename E::Scalar* GScalar;
+    uint32_t tbits = 0xFFFFFFFFu;
+    auto first_loads = [&](bool) {
+        load(0, xa);
+        load(kR, xc);
+        if ((int64_t)threadIdx.x < L - tail0) tbits = E::scalar_bits(((GScalar)row)[tail0 + threadIdx.x]);
     };
     static_assert(kShortCap <= kR * E::kPerVec, "one round covers a row that keeps every score");
     Cutoff cut{0u, 0xFFFFFFFFu};  // a row that keeps every score has no sample
-    if (keep_all) load(0, xa);
-    else cut = short_cutoff<E>(row, L, m, reinterpret_cast<uint32_t*>(buf), lds, first_loads);
-    const uint32_t T = cut.T;
-    B::sync();  // the sample's keys are read; the buffer takes survivors now
+    if (keep_all) first_loads(false);
+    else cut = short_cutoff<E>(row, L, m, lds, first_loads);
+    // Raising a cutoff below kMinT changes nothing for non-NaN scores (all
+    // pass either way) and lets the padded loads fail the survivor test.
+    const uint32_t T = max(cut.T, kMinT);
+    const bool pos = T >= 0x80000000u;  // at or above the key of +0
+    const SurvivorBound sb = E::bound(T, pos);
 
-    auto filter = [&](const Vec (&x)[kU], int64_t base) {
+    // One round: each lane counts its survivors, one LDS reservation per wave
+    // places them (a wave that would pass the capacity writes nothing; the
+    // count still grows, so the row then takes the full-row selection), and
+    // each lane writes its survivors to consecutive slots. Every lane writes
+    // for every score, a failing one to the lane's spare entry, so that the
+    // writes need no branches.
+    auto filter = [&](auto pos_tag, const Vec (&x)[kU], int64_t base) {
+        constexpr bool kPos = decltype(pos_tag)::value;
         uint32_t cnt = 0u;
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const bool in = base + u * kThreads + threadIdx.x < nvec;
 #pragma unroll
-            for (int j = 0; j < E::kPerVec; ++j) cnt += (in && elem_key<E>(E::bits(x[u], j)) >= T) ? 1u : 0u;
+            for (int j = 0; j < E::kPerVec; ++j) {
+                uint32_t bits;
+                cnt += E::template pass<kPos>(x[u], j, sb, bits) ? 1u : 0u;
+            }
         }
-        uint32_t slot = wave_reserve_count(&count, cnt);
-        if (cnt != 0u) {
+        const uint32_t incl = wave_inclusive_sum(cnt);
+        const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+        if (total == 0u) return;
+        uint32_t wbase = 0u;
+        if (lane_id() == 0) wbase = atomicAdd(&count, total);
+        wbase = __builtin_amdgcn_readfirstlane(wbase);
+        if (wbase + total > cap) return;
+        // byte offsets into the buffer: the lane's next slot and its spare
+        uint32_t slot = (wbase + incl - cnt) * (uint32_t)sizeof(uint2);
+        const uint32_t spare = ((uint32_t)kShortCap + lane_id()) * (uint32_t)sizeof(uint2);
+        char* const bytes = reinterpret_cast<char*>(buf);
+        const uint32_t p0 = (uint32_t)(E::kPerVec * (base + threadIdx.x));
+        // The tests run again here rather than keep 32 results per lane live
+        // across the reservation: the bounds are taken through wbase >> 31,
+        // always 0 (counts stay below 2^31) but not known to the compiler.
+        const uint32_t z = wbase >> 31;
+        const SurvivorBound sb2{sb.t ^ z, sb.th ^ z};
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int64_t g = base + u * kThreads + threadIdx.x;
+        for (int u = 0; u < kU; ++u) {
 #pragma unroll
-                for (int j = 0; j < E::kPerVec; ++j) {
-                    const uint32_t bits = E::bits(x[u], j);
-                    if (g < nvec && elem_key<E>(bits) >= T) {
-                        if (slot < cap) buf[slot] = make_uint2(bits, (uint32_t)(E::kPerVec * g + j));
-                        ++slot;
-                    }
-                }
+            for (int j = 0; j < E::kPerVec; ++j) {
+                uint32_t bits;
+                const bool ok = E::template pass<kPos>(x[u], j, sb2, bits);
+                *reinterpret_cast<uint2*>(bytes + (ok ? slot : spare)) =
+                    make_uint2(bits, p0 + (uint32_t)(E::kPerVec * kThreads * u + j));
+                slot += ok ? (uint32_t)sizeof(uint2) : 0u;
             }
         }
     };
-    int64_t base = 0;
-    while (base < nvec) {  // uniform over the workgroup
-        if (base > 0 && base + kR < nvec) load(base + kR, xc);  // round 1 is in flight already
-        filter(xa, base);
-        base += kR;
-        if (base >= nvec) break;
-        if (base + kR < nvec) load(base + kR, xa);
-        filter(xc, base);
-        base += kR;
-    }
-    if (nvec * E::kPerVec < L && threadIdx.x < 64) {  // the scores past the last full load
-        const int64_t i = nvec * E::kPerVec + threadIdx.x;
-        const uint32_t bits = i < L ? E::scalar_bits(row[i]) : 0u;
-        const bool hit = i < L && elem_key<E>(bits) >= T;
+    // The first two rounds are in flight since the sample; a third is loaded
+    // into the first buffer as soon as that has been filtered. Rows past
+    // three rounds (wider than any the short-row path is fast for) go on one
+    // round at a time.
+    auto stream = [&](auto pos_tag) {
+        filter(pos_tag, xa, 0);
+        if (kR >= nvec) return;
+        if (2 * kR < nvec) load(2 * kR, xa);
+        filter(pos_tag, xc, kR);
+        for (int64_t base = 2 * kR; base < nvec; base += kR) {  // uniform over the workgroup
+            if (base > 2 * kR) load(base, xa);
+            filter(pos_tag, xa, base);
+        }
+    };
+    if (pos) stream(std::true_type{});
+    else stream(std::false_type{});
+    if (tail0 < L && wave_id() == 0) {
+        const bool hit = pos ? (int32_t)tbits >= (int32_t)sb.t : tbits <= sb.t;  // exact widened bits
         const uint32_t slot = wave_reserve_count(&count, hit ? 1u : 0u);
-        if (hit && slot < cap) buf[slot] = make_uint2(bits, (uint32_t)i);
+        if (hit && slot < cap) buf[slot] = make_uint2(tbits, (uint32_t)(tail0 + threadIdx.x));
     }
     B::sync();
     const uint32_t n = count;
@@ -753,9 +1053,58 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         emit(src, s, out);
     } else {
         code = keep_all ? TOPK_ROW_LDS : TOPK_ROW_SAMPLED;
-        const PairSource<B> src{buf, n};
-        const Selection s = short_select<E, B>(lds, src, m, n, T, cut.hi, bits_for(L), ties);
-        emit(src, s, out);
+        // A paged row's page-table entries, when they fit the histogram, are
+        // loaded now (their latency hidden by the selection) and staged there
+        // once the selection is done with it.
+        constexpr int kPg = kBins / kThreads;
+        const int32_t* pages = p.page_table ? p.page_table + b * p.pt_stride : nullptr;
+        const bool pow2 = (p.page_size & (p.page_size - 1)) == 0;
+        const uint32_t npg = pages ? (uint32_t)((((uint64_t)(L - 1) * p.page_magic) >> p.page_shift) + 1u) : 0u;
+        const bool stage = pow2 && npg != 0u && npg <= (uint32_t)kBins;
+        int32_t pg[kPg];
+        if (stage) {
+#pragma unroll
+            for (int i = 0; i < kPg; ++i) {
+                const uint32_t t = (uint32_t)(i * kThreads) + threadIdx.x;
+                if (t < npg) pg[i] = pages[t];
+            }
+        }
+        // the survivors into registers, every read in flight at once (the LDS
+        // buffer then holds the tie regions; the selection's first barrier
+        // orders the two uses)
+        constexpr int kSlots = (kShortCap + kThreads - 1) / kThreads;
+        static_assert(kSlots * kThreads <= kShortCap + 64, "every slot reads inside the buffer");
+        RegPairs<kSlots> sv;
+        sv.nslot = (int)((n + kThreads - 1) / kThreads);
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const uint32_t e = (uint32_t)(i * kThreads) + threadIdx.x;
+            const uint2 v = buf[e];
+            sv.bits[i] = e < n ? v.x : 0xFFFFFFFFu;
+            sv.idx[i] = e < n ? v.y : 0xFFFFFFFFu;
+        }
+        const SurvSel s = short_select<E, B>(lds, sv, m, n, T, cut.hi, bits_for(L));
+        if (stage) {  // the selection has left the histogram (the emission syncs before reading)
+#pragma unroll
+            for (int i = 0; i < kPg; ++i) {
+                const uint32_t t = (uint32_t)(i * kThreads) + threadIdx.x;
+                if (t < npg) reinterpret_cast<int32_t*>(hist)[t] = pg[i];
+            }
+        }
+        int32_t* row = p.out + b * (int64_t)p.k;
+        uint32_t* tw = reinterpret_cast<uint32_t*>(buf);
+        static_assert(emit_words<kThreads / 64>() <= 2 * (kShortCap + 64), "the emission fits the buffer");
+        // Without a page table the staged map is the identity: with l = 31,
+        // every position reads hist[0], which the selection left at 0. (Two
+        // variants, not three: with a third, the compiler keeps the survivor
+        // registers in scratch memory.)
+        if (pages == nullptr || stage)
+            emit_slots<B>(sv, s, m, row,
+                          LdsShiftMap{(LdsI32)reinterpret_cast<const int32_t*>(hist),
+                                      pages == nullptr ? 31u : (uint32_t)(31 - __clz(p.page_size))},
+                          bits_for(L), wtot, tw);
+        else
+            emit_slots<B>(sv, s, m, row, global_map(p, b), bits_for(L), wtot, tw);
     }
     if (threadIdx.x == 0) split_stats(p, b, code, n);
 }
@@ -770,7 +1119,9 @@ int launch_short(const void* scores, int64_t batch, int64_t row_stride, int64_t 
     const int32_t cap = opt.capacity == 0 ? kShortCap : opt.capacity;
     if (cap < 1 || cap > kShortCap) return TOPK_ERR_ARG;
     SplitParams p{static_cast<const float*>(scores), row_stride, n_cols, lengths, out_idx, page_table,
-                  page_table_stride, page_size, k, opt.force_path, cap, opt.row_stats, batch, nullptr, nullptr, 0, 1};
+                  page_table_stride, page_size, k, opt.force_path, cap, opt.row_stats, batch, nullptr, nullptr, 0, 1,
+                  0u, 0};
+    page_divider(page_table != nullptr ? page_size : 1, p.page_magic, p.page_shift);
     void* args[] = {&p};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&short_rows_kernel<E>), dim3((uint32_t)batch),
                                          dim3(kThreads), args, 0, stream);
@@ -872,7 +1223,8 @@ int split_select(const float* scores, int64_t batch, int64_t row_stride, int64_t
     SplitParams p{scores, row_stride, n_cols, lengths, out_idx, page_table, page_table_stride, page_size, k,
                   opt.force_path, opt.capacity, opt.row_stats, batch,
                   reinterpret_cast<SplitHead*>(ws), reinterpret_cast<uint2*>(ws + head_bytes(batch)),
-                  per, (int32_t)P};
+                  per, (int32_t)P, 0u, 0};
+    page_divider(page_table != nullptr ? page_size : 1, p.page_magic, p.page_shift);
     void* args[] = {&p};
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     if (hipLaunchKernel(reinterpret_cast<const void*>(&split_sample_kernel), dim3((uint32_t)batch), dim3(kThreads),

@@ -387,16 +387,23 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
     }
     constexpr int kVecPerRun = kRunLen / E::kPerVec;
     constexpr int kPer = kMaxSample / E::kPerVec / kThreads;  // loads per lane, all in flight
+    constexpr int kLineVecs = 128 / 16;                       // loads per 128-byte line
     const int nsv = runs * kVecPerRun;
     const int64_t span = L - kRunLen;
     const typename E::Vec* rv = reinterpret_cast<const typename E::Vec*>(row);
+    // the row's first load lies `lead` loads into its 128-byte line
+    const int64_t lead = (int64_t)((reinterpret_cast<uintptr_t>(row) & 127u) >> 4);
     typename E::Vec x[kPer];
 #pragma unroll
     for (int h = 0; h < kPer; ++h) {
         const int t = h * kThreads + (int)threadIdx.x;
         const int r = t / kVecPerRun;
-        // run r starts at floor(r * span / (runs - 1)), rounded down to a load
-        const int64_t start = ((int64_t)r * span / (runs - 1)) / E::kPerVec;
+        // run r starts near floor(r * span / (runs - 1)), moved down to the
+        // start of a 128-byte line (a run of 64 scores then covers whole
+        // lines only; the first run stays at 0 when that would go below it)
+        int64_t start = ((int64_t)r * span / (runs - 1)) / E::kPerVec;
+        start = (start + lead) / kLineVecs * kLineVecs - lead;
+        start = start < 0 ? 0 : start;
         if (t < nsv) x[h] = rv[start + t % kVecPerRun];
     }
     issue(true);
@@ -434,11 +441,6 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
     }
     const uint32_t q = (want + kThreads - 1) / kThreads;
     const bool one_pass = want > 0u && q <= (uint32_t)kQ;  // uniform
-    // With q <= kQ the histograms take only each lane's kQ largest keys (0
-    // for a lane with fewer): a subset of the sample, so its want-th largest
-    // key is at or below the sample's and T stays a valid cutoff; it is
-    // lower only by the keys of lanes holding more than kQ above it.
-    const RegKeys<1, kQ> cand{top, kThreads};
     __shared__ uint32_t s_lo, s_hi;
     if (threadIdx.x == 0) {
         s_lo = 0xFFFFFFFFu;
@@ -465,7 +467,7 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
         const uint32_t lo = s_lo, hi = max(shi, lo);
         const int sh = bin_shift(hi - lo);
         const uint32_t base = lo & ~((1u << sh) - 1u);  // (hi - base) >> sh <= kBins - 2
-        const Cut c = radix_select_slots<B>(lds, cand, SampleBinView{lo, hi, base, sh}, want, 0u, kDigitBits, n);
+        const Cut c = radix_select_slots<B>(lds, keys, SampleBinView{lo, hi, base, sh}, want, 0u, kDigitBits, n);
         if (c.value == (uint32_t)(kBins - 1)) return Cutoff{hi + 1u, shi};
         const uint32_t edge = base + (c.value << sh);
         // A few far keys (peaks well above a dense bulk) stretch [lo, hi] so
@@ -477,7 +479,7 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
         if (sh > 0 && 4u * (c.equal - c.need) > want) {
             const int sh2 = sh > kDigitBits - 1 ? sh - (kDigitBits - 1) : 0;
             const uint32_t bin_top = min(edge + ((1u << sh) - 1u), hi);  // no overflow: hi < +inf's key
-            const Cut c2 = radix_select_slots<B>(lds, cand, SubBinView{edge, max(edge, lo), bin_top, sh2},
+            const Cut c2 = radix_select_slots<B>(lds, keys, SubBinView{edge, max(edge, lo), bin_top, sh2},
                                            c.need, 0u, kDigitBits, c.equal);
             return Cutoff{edge + (c2.value << sh2), shi};
         }
@@ -1173,6 +1175,8 @@ int scratch_address(void** ptr) {
 
 // topk_select_split's checks and launches; with use_scratch, the workspace
 // is the library's scratch array, looked up once every argument has passed.
+inline bool options_default_capacity(const topk_options* o) { return o == nullptr || o->capacity == 0; }
+
 int split_select(const float* scores, int64_t batch, int64_t row_stride, int64_t n_cols, const int32_t* lengths,
                  int32_t k, int32_t* out_idx, const int32_t* page_table, int64_t page_table_stride,
                  int32_t page_size, void* workspace, int64_t workspace_bytes, int32_t pieces, void* hip_stream,
@@ -1198,11 +1202,19 @@ int split_select(const float* scores, int64_t batch, int64_t row_stride, int64_t
     if (!use_scratch && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TOPK_ERR_ALIGN;
     if (batch > 1 && (row_stride & 3) != 0) return TOPK_ERR_ALIGN;
     // pieces per row: enough workgroups for about four per compute unit, each
-    // piece a whole number of load rounds
+    // piece a whole number of load rounds. A batch that already brings four
+    // rows per compute unit gets one piece per row, and then one workgroup
+    // per row in a single launch (topk_select's kernels) does the same work
+    // without the survivors' round trip through the workspace, which is left
+    // untouched (only with the default capacity, whose bound both paths
+    // accept).
     int64_t want = pieces;
     if (want == 0) {
         const int cus = device_cus();
         if (cus <= 0) return TOPK_ERR_DEVICE;
+        if (!use_scratch && options_default_capacity(options) && batch >= 4 * (int64_t)cus)
+            return topk_select_ex(scores, batch, row_stride, n_cols, lengths, k, out_idx, page_table,
+                                  page_table_stride, page_size, hip_stream, options);
         want = (4 * (int64_t)cus + batch - 1) / batch;
     }
     const int64_t nvec_max = (n_cols + 3) / 4;

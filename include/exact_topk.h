@@ -191,7 +191,11 @@ uint32_t topk_watchdog_trips(void);
  *  pieces           workgroups per row wanted, 0 = about four workgroups per
  *                   compute unit over the batch, at most 256; each piece is a
  *                   whole number of 8192-score rounds, so short rows get
- *                   fewer pieces
+ *                   fewer pieces. With 0, a batch of at least four rows per
+ *                   compute unit (one piece per row) runs as topk_select_ex
+ *                   does, one workgroup per row in one launch, and the
+ *                   workspace is not touched (unless options set a
+ *                   capacity: then the split kernels run)
  *  options          as for topk_select_ex, with capacity up to
  *                   topk_split_capacity() and kernel TOPK_KERNEL_AUTO (this
  *                   entry has its own kernels); TOPK_PATH_LDS keeps every score of

@@ -133,12 +133,22 @@ def test_split_small_batches_of_the_decode_rows(topk, c3, c4, batch):
 
 
 def test_split_full_decode_batches(topk, c3, c4):
+    # one piece per row through the split kernels; then the automatic piece
+    # count, which on batches of four rows per compute unit runs one
+    # workgroup per row in one launch and leaves the workspace untouched
     for wl in (c3, c4):
-        got, stats = run_split(topk, wl, want_stats=True)
-        bad = check_fast_raw(got, expect(wl), wl.lengths, wl.n_cols, wl.k)
+        want = expect(wl)
+        got, stats = run_split(topk, wl, pieces=1, want_stats=True)
+        bad = check_fast_raw(got, want, wl.lengths, wl.n_cols, wl.k)
         assert not bad, f"rows differing from the oracle: {bad[:10]}"
         say(f"  {wl.name} split paths:", dict(zip(*np.unique(stats[:, 0], return_counts=True))),
             "survivors mean/max:", stats[:, 1].mean(), stats[:, 1].max())
+        ws = guarded_workspace(topk, wl.batch, 0xA7)
+        got, _ = run_split(topk, wl, pieces=0, workspace=ws)
+        bad = check_fast_raw(got, want, wl.lengths, wl.n_cols, wl.k)
+        assert not bad, f"rows differing from the oracle: {bad[:10]}"
+        if wl.batch >= 4 * torch.cuda.get_device_properties(0).multi_processor_count:
+            assert bool((ws[1] == 0xA7).all()), "the one-workgroup-per-row launch wrote to the workspace"
 
 
 @pytest.mark.parametrize("global_pool", [False, True], ids=["row_perm", "global_pool"])

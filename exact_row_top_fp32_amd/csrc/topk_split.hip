@@ -55,7 +55,8 @@ constexpr int kThreads = 256;                   // 4 waves per workgroup
 constexpr int kUnroll = 8;                      // 16-byte loads per lane per round
 constexpr int64_t kRound = kThreads * kUnroll;  // 4-score groups per workgroup round (32 KB)
 constexpr int kRunLen = 64;                     // scores per contiguous sample run
-constexpr int kMaxRuns = 64;
+constexpr int kMaxRuns = 64;                    // sample runs of a split row
+constexpr int kShortRuns = 32;                  // sample runs of a short row
 constexpr int kMaxSample = kRunLen * kMaxRuns;  // 4096 keys at most
 constexpr int kMaxPieces = 256;                 // workgroups per row at most
 constexpr int kFinThreads = 1024;               // finisher workgroup: 16 waves
@@ -363,6 +364,10 @@ struct SubBinView {
 // too few keys for that bound, the lowest key of its top 22 bits (two 11-bit
 // digits, at most 2^10 keys below it).
 //
+// The sample has at most kRuns runs: 64 for the split rows, 32 for short
+// rows, where the sample's own work is a larger part of the row's (2048 keys
+// of a 16384-score row still leave the survivors at about 1.1 m for m = 2048).
+//
 // `issue(true)` runs right after the sample's loads are issued (`issue(false)`
 // on the early return of a row too short to sample), so that a caller's own
 // loads are in flight while the cutoff is found.
@@ -375,18 +380,19 @@ struct Cutoff {
     uint32_t hi;  // the sample's largest key below +inf's (0xFFFFFFFF: no sample)
 };
 
-template <class E, class Issue = NoIssue>
+template <class E, int kRuns = kMaxRuns, class Issue = NoIssue>
 __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, SelectLds lds,
                                Issue&& issue = Issue{}) {
     using B = BlockScope<kThreads>;
     const int64_t fit = L / (2 * kRunLen);
-    const int runs = fit < kMaxRuns ? (int)fit : kMaxRuns;
+    const int runs = fit < kRuns ? (int)fit : kRuns;
     if (runs < 2) {
         issue(false);
         return Cutoff{0u, 0xFFFFFFFFu};
     }
     constexpr int kVecPerRun = kRunLen / E::kPerVec;
-    constexpr int kPer = kMaxSample / E::kPerVec / kThreads;  // loads per lane, all in flight
+    constexpr int kPer = kRuns * kRunLen / E::kPerVec / kThreads;  // loads per lane, all in flight
+    static_assert(kPer >= 1 && kPer * E::kPerVec * kThreads == kRuns * kRunLen, "whole loads per lane");
     constexpr int kLineVecs = 128 / 16;                       // loads per 128-byte line
     const int nsv = runs * kVecPerRun;
     const int64_t span = L - kRunLen;
@@ -970,7 +976,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     static_assert(kShortCap <= kR * E::kPerVec, "one round covers a row that keeps every score");
     Cutoff cut{0u, 0xFFFFFFFFu};  // a row that keeps every score has no sample
     if (keep_all) first_loads(false);
-    else cut = short_cutoff<E>(row, L, m, lds, first_loads);
+    else cut = short_cutoff<E, kShortRuns>(row, L, m, lds, first_loads);
     // Raising a cutoff below kMinT changes nothing for non-NaN scores (all
     // pass either way) and lets the padded loads fail the survivor test.
     const uint32_t T = max(cut.T, kMinT);

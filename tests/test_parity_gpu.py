@@ -594,14 +594,16 @@ def test_short_rows_infinities(topk, n_inf, k):
 # a sample that sees only the peaks: survivors fall short of m
 # ----------------------------------------------------------------------------
 
-def sample_positions(L):
-    """Where every sampling path reads a row of length L: runs of 64 scores at
-    floor(r (L - 64) / (runs - 1)) rounded down to a multiple of 4,
-    runs = min(L // 128, 64)."""
-    runs = min(L // 128, 64)
+def sample_positions(L, max_runs, align):
+    """Where a sampling path reads a row of length L: runs of 64 scores at
+    floor(r (L - 64) / (runs - 1)) rounded down to a multiple of `align`,
+    runs = min(L // 128, max_runs). The persistent kernel takes 64 runs on
+    16-byte loads (align 4); the short-row kernel 32 runs on 128-byte lines
+    (align 32 here, where every row starts on a line)."""
+    runs = min(L // 128, max_runs)
     pos = []
     for r in range(runs):
-        start = (r * (L - 64) // (runs - 1)) & ~3
+        start = (r * (L - 64) // (runs - 1)) // align * align
         pos.extend(range(start, start + 64))
     return np.array(pos, np.int64)
 
@@ -616,8 +618,15 @@ def test_sample_that_sees_only_peaks_underflows(topk, W, k):
     B = 4
     scores = rng.standard_normal((B, W)).astype(np.float32)
     lengths = np.array([W, W - 3, W - 17, W], np.int32)
+    # peaks where both this row's kernel and the split-row entry (64 runs on
+    # 128-byte lines) sample; every row starts on a 128-byte line
+    short = W <= 32768
+    assert (W * 4) % 128 == 0
     for b in range(B):
-        pos = sample_positions(int(lengths[b]))
+        L = int(lengths[b])
+        pos = np.intersect1d(sample_positions(L, 32 if short else 64, 32 if short else 4),
+                             sample_positions(L, 64, 32))
+        assert pos.size >= k // 2
         hit = rng.choice(pos, min(k // 2, pos.size), replace=False)
         scores[b, hit] = (50.0 + rng.standard_normal(hit.size)).astype(np.float32)
     synth.poison_tails(scores, lengths)
@@ -630,7 +639,7 @@ def test_sample_that_sees_only_peaks_underflows(topk, W, k):
         got, stats = run(topk, wl, force=2, want_stats=True)
         assert_parity(wl, got, want)
         assert np.all(stats[:, 0] == 5)
-    # the split-row entry samples the same positions
+    # the split-row entry's sample sees the same peaks
     buf = torch.full((B, k), CANARY, dtype=torch.int32, device="cuda")
     sstats = torch.full((B, 2), -7, dtype=torch.int32, device="cuda")
     topk.topk_select_split(to_dev(wl.scores), to_dev(wl.lengths), k, buf, row_stats=sstats)

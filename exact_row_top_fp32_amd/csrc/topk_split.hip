@@ -151,15 +151,16 @@ struct RegKeys {
 };
 
 // Survivors held in registers, N slots per lane: slot i of a lane holds the
-// raw score bits and the position of one survivor, or all-ones bits and the
-// position 0xFFFFFFFF (no survivor; positions are below 2^31). Slots at or
+// order key and the position of one survivor, or key 0 and the position
+// 0xFFFFFFFF (no survivor; positions are below 2^31, and key 0 lies below
+// every cutoff, which is at least kMinT). Slots at or
 // past `nslot` are empty on every lane. Slots are visited in groups of
 // kGroup, a group wholly past nslot skipped by one uniform test (a test per
 // slot would hold a mask register per slot).
 constexpr int kGroup = 4;
 template <int N>
 struct RegPairs {
-    uint32_t bits[N];
+    uint32_t key[N];
     uint32_t idx[N];
     int nslot;
     template <class F>
@@ -174,7 +175,7 @@ struct RegPairs {
     }
     template <class F>
     __device__ __forceinline__ void for_each_slot(F&& f) const {
-        for_each_group([&](int i) { f(order_key(__uint_as_float(bits[i])), idx[i], idx[i] != 0xFFFFFFFFu); });
+        for_each_group([&](int i) { f(key[i], idx[i], idx[i] != 0xFFFFFFFFu); });
     }
 };
 
@@ -632,32 +633,79 @@ struct ShiftedRangeView {
     }
 };
 
-// A selection among survivors: keys above kth are taken; keys equal to kth
-// are taken when their position is at most icut, or, with need > 0, the
-// need lowest positions of the `equal` (at most 64) tied survivors are.
-struct SurvSel {
-    uint32_t kth;
-    int32_t icut;
-    uint32_t need;
-    uint32_t equal;
-    __device__ static SurvSel of(Selection s) { return SurvSel{s.kth, s.icut, 0u, 0u}; }
-};
+// The members of a cutoff bin, at most 64 survivors whose shifted keys lie in
+// [lo_x, hi_x], ranked directly. They are gathered into LDS (`mem`: 64
+// entries, then a spare entry per lane; `*mcount` zero on entry) as the
+// filter appends survivors: per-lane counts, one reservation per wave,
+// writes without branches. Then one wave holds a member per lane and ranks
+// each by key, largest first, and position, lowest first, against every
+// other (read across lanes); the member of rank need - 1 gives the cutoff
+// key and the last position taken at it. This replaces a radix pass over
+// the positions and any ranking of ties in the emission.
+template <class B, int N, int kShift>
+__device__ __forceinline__ Selection rank_members(const RegPairs<N>& sv, uint32_t lo_x, uint32_t hi_x,
+                                                  uint32_t need, uint2* mem, uint32_t* mcount, uint2* pick) {
+    auto member = [&](int i, uint32_t& key) {
+        key = sv.key[i];
+        const uint32_t x = key >> kShift;
+        return (sv.idx[i] != 0xFFFFFFFFu) & (x >= lo_x) & (x <= hi_x);
+    };
+    uint32_t cnt = 0u;
+    sv.for_each_group([&](int i) {
+        uint32_t key;
+        cnt += member(i, key) ? 1u : 0u;
+    });
+    const uint32_t incl = wave_inclusive_sum(cnt);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    if (total != 0u) {
+        uint32_t wbase = 0u;
+        if (lane_id() == 0) wbase = atomicAdd(mcount, total);
+        uint32_t at = __builtin_amdgcn_readfirstlane(wbase) + incl - cnt;
+        const uint32_t spare = (uint32_t)kMaxCand + lane_id();
+        sv.for_each_group([&](int i) {
+            uint32_t key;
+            const bool in = member(i, key);
+            mem[(in & (at < (uint32_t)kMaxCand)) ? at : spare] = make_uint2(key, sv.idx[i]);
+            at += in ? 1u : 0u;
+        });
+    }
+    B::sync();
+    if (B::first_wave()) {
+        const uint32_t ne = __builtin_amdgcn_readfirstlane(min(*mcount, (uint32_t)kMaxCand)), lane = lane_id();
+        const uint2 me = lane < ne ? mem[lane] : make_uint2(0u, 0xFFFFFFFFu);
+        uint32_t rank = 0u;
+        if (lo_x == hi_x) {  // one key (a shifted key fixes the full one): by position alone
+            for (uint32_t j = 0; j < ne; ++j)
+                rank += (uint32_t)__builtin_amdgcn_readlane((int)me.y, (int)j) < me.y ? 1u : 0u;
+        } else {
+            for (uint32_t j = 0; j < ne; ++j) {
+                const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)me.x, (int)j);
+                const uint32_t op = (uint32_t)__builtin_amdgcn_readlane((int)me.y, (int)j);
+                rank += ((ok > me.x) | ((ok == me.x) & (op < me.y))) ? 1u : 0u;
+            }
+        }
+        if ((lane < ne) & (rank == need - 1u)) *pick = me;
+    }
+    B::sync();
+    const uint2 w = *pick;
+    return Selection{w.x, (int32_t)w.y};
+}
 
-// Exact top m of a row's survivors held in LDS by workgroup scope B (keys at
-// least T; the short-row and split-finish kernels), ties at the cutoff to the
-// lowest positions, as select_top does, with three savings. Keys are
-// selected on key >> E::kKeyShift, which drops only bits that carry no
-// information (bf16: 16-bit keys). The first pass bins [T, hi] into at most
-// 2047 bins of equal width (a power of two), keys above hi in a top bin of
-// their own, so the survivors spread over many bins instead of the few that
-// their top 11 bits share (bins of width 1 settle the cutoff in that pass);
-// hi need not bound every survivor (the sample's largest finite key serves),
-// and +inf does not stretch the bins. And when at most 64 survivors equal
-// the cutoff key and only some of them are taken, the emission ranks their
-// positions (SurvSel::need) instead of radix passes over the positions.
-template <class E, class B, class Src>
-__device__ SurvSel short_select(SelectLds lds, const Src& src, uint32_t m, uint32_t n, uint32_t T, uint32_t hi_key,
-                                int idx_bits) {
+// Exact top m of a row's survivors held in registers by workgroup scope B
+// (keys at least T; the short-row and split-finish kernels), ties at the
+// cutoff to the lowest positions, as select_top does, with three savings.
+// Keys are selected on key >> E::kKeyShift, which drops only bits that carry
+// no information (bf16: 16-bit keys). The first pass bins [T, hi] into at
+// most 2047 bins of equal width (a power of two), keys above hi in a top bin
+// of their own, so the survivors spread over many bins instead of the few
+// that their top 11 bits share (bins of width 1 settle the cutoff in that
+// pass); hi need not bound every survivor (the sample's largest finite key
+// serves), and +inf does not stretch the bins. And a cutoff bin of at most
+// 64 survivors is ranked directly (rank_members) instead of by further radix
+// passes. `mem` (64 + 64 entries), `mcount` and `pick` are rank_members' LDS.
+template <class E, class B, int N>
+__device__ Selection short_select(SelectLds lds, const RegPairs<N>& src, uint32_t m, uint32_t n, uint32_t T,
+                                  uint32_t hi_key, int idx_bits, uint2* mem, uint32_t* mcount, uint2* pick) {
     constexpr int kShift = E::kKeyShift;
     constexpr uint32_t kTop = 0xFFFFFFFFu >> kShift;
     const uint32_t lo = T >> kShift, hi = max(hi_key >> kShift, lo);
@@ -666,28 +714,33 @@ __device__ SurvSel short_select(SelectLds lds, const Src& src, uint32_t m, uint3
     const Cut c1 = radix_select_slots<B>(lds, src, AboveBinView<kShift>{base, hi, sh}, m, 0u, kDigitBits, n);
     Cut c;
     if (c1.value == (uint32_t)(kBins - 1)) {  // the cutoff is above hi (so hi < kTop)
-        if (c1.need == c1.equal) return SurvSel::of(at_least((hi + 1u) << kShift));
+        if (c1.need == c1.equal) return at_least((hi + 1u) << kShift);
+        if (c1.equal <= (uint32_t)kMaxCand)
+            return rank_members<B, N, kShift>(src, hi + 1u, kTop, c1.need, mem, mcount, pick);
         c = radix_select_slots<B>(lds, src, ShiftedRangeView<kShift>{hi + 1u, kTop}, c1.need, 0u, 32 - kShift,
                                   c1.equal);
-        if (c.range) return SurvSel::of(at_least(c.value << kShift));
+        if (c.range) return at_least(c.value << kShift);
     } else {
         const uint32_t edge = base + (c1.value << sh);  // lowest value in the cutoff bin
-        if (c1.need == c1.equal) return SurvSel::of(at_least(edge << kShift));  // the bin is taken whole
+        if (c1.need == c1.equal) return at_least(edge << kShift);  // the bin is taken whole
+        // the bin's keys share the bits above sh; keys above hi with those
+        // bits were counted in the top bin, so they stay out
+        const uint32_t bin_hi = min(edge + ((1u << sh) - 1u), hi);
+        if (c1.equal <= (uint32_t)kMaxCand)
+            return rank_members<B, N, kShift>(src, edge, bin_hi, c1.need, mem, mcount, pick);
         c = Cut{edge, c1.need, c1.equal, false};
         if (sh > 0) {
-            // the bin's keys share the bits above sh; keys above hi with
-            // those bits were counted in the top bin, so they stay out
             c = radix_select_slots<B>(lds, src, ShiftedRangeView<kShift>{edge, hi}, c1.need, edge, sh, c1.equal);
-            if (c.range) return SurvSel::of(at_least(c.value << kShift));  // the least full key whose top bits reach c.value
+            if (c.range) return at_least(c.value << kShift);  // the least full key whose top bits reach c.value
         }
     }
     const uint32_t kth = E::full_key(c.value);
-    if (c.need >= c.equal) return SurvSel{kth, INT32_MAX, 0u, 0u};
-    if (c.equal <= (uint32_t)kMaxCand) return SurvSel{kth, 0, c.need, c.equal};  // ranked by the emission
+    if (c.need >= c.equal) return Selection{kth, INT32_MAX};
+    if (c.equal <= (uint32_t)kMaxCand) return rank_members<B, N, kShift>(src, c.value, c.value, c.need, mem, mcount, pick);
     // the need-th largest inverted index among the ties (select_top's way)
     const uint32_t iprefix = idx_bits >= 32 ? 0u : (0xFFFFFFFFu << idx_bits);
     const Cut t = radix_select_slots<B>(lds, src, TieIndexView{kth}, c.need, iprefix, idx_bits, c.equal);
-    return SurvSel{kth, (int32_t)(~t.value), 0u, 0u};
+    return Selection{kth, (int32_t)(~t.value)};
 }
 
 // Positions to output values: the identity, or the page-table transform
@@ -723,99 +776,45 @@ __device__ __forceinline__ GlobalMagicMap global_map(const SplitParams& p, int64
                           p.page_shift};
 }
 
-// LDS words the emission works in: the output list (m <= TOPK_MAX_K entries,
-// then one spare word per lane), then each wave's 64-word tie region, then
-// one spare word per lane for the ties.
+// LDS words the emission works in: the output list (m <= TOPK_MAX_K entries),
+// then one spare word per lane.
 constexpr int kListWords = TOPK_MAX_K + 64;
-template <int kWaves>
-constexpr int emit_words() { return kListWords + 64 * kWaves + 64; }
 
-// Writes the survivors a SurvSel takes, from the registers that hold them.
+// Writes the survivors a Selection takes, from the registers that hold them.
 // Each lane counts the entries it takes; a wave prefix sum and the waves'
 // totals give every lane its run of places in an LDS list, where the lanes
 // write their entries already mapped (an entry not taken goes to the lane's
 // spare word, so no write branches); after a barrier the list is copied to
-// the output row, coalesced. Ranked ties (SurvSel::need > 0): each lane
-// writes its tied positions to its wave's 64-word tie region in the same
-// way, and one wave finds the need-th smallest of the `equal` (<= 64) of
-// them, bit by bit from the top of idx_bits, and lists the need lowest after
-// the rest. The work is vector instructions with few scalar round trips, so
-// that a lone wave per SIMD is not held up between them. wtot holds two
-// words per wave; ws emit_words<kWaves>() words. A selection holds exactly m
-// entries; the bounds only keep a defect from writing outside the row or
-// the LDS areas.
+// the output row, coalesced. The work is vector instructions with few scalar
+// round trips, so that a lone wave per SIMD is not held up between them.
+// wtot holds a word per wave; lst kListWords words. A selection holds
+// exactly m entries; the bounds only keep a defect from writing outside the
+// row or the list.
 template <class B, int N, class Map>
-__device__ __forceinline__ void emit_slots(const RegPairs<N>& sv, SurvSel sel, uint32_t m, int32_t* row,
-                                           const Map& map, int idx_bits, uint32_t* wtot, uint32_t* ws) {
+__device__ __forceinline__ void emit_slots(const RegPairs<N>& sv, Selection sel, uint32_t m, int32_t* row,
+                                           const Map& map, uint32_t* wtot, uint32_t* lst) {
     constexpr int kWaves = B::kSize / 64;
     const uint32_t w = wave_id(), lane = lane_id();
-    uint32_t* lst = ws;
-    uint32_t* tw = ws + kListWords;
-    // an empty slot holds all-ones bits, key 0, below every cutoff key (at
-    // least kMinT), so it is neither taken nor tied
-    const bool by_icut = sel.need == 0u;
-    auto look = [&](int i, bool& tie) {
-        const uint32_t key = order_key(__uint_as_float(sv.bits[i]));
-        tie = (key == sel.kth) & !by_icut;
-        return (key > sel.kth) | ((key == sel.kth) & by_icut & ((int32_t)sv.idx[i] <= sel.icut));
+    // an empty slot holds key 0, below every cutoff key, so it is never taken
+    auto take = [&](int i) {
+        const uint32_t key = sv.key[i];
+        return (key > sel.kth) | ((key == sel.kth) & ((int32_t)sv.idx[i] <= sel.icut));
     };
-    uint32_t cnt = 0u, tcnt = 0u;
-    sv.for_each_group([&](int i) {
-        bool tie;
-        cnt += look(i, tie) ? 1u : 0u;
-        tcnt += tie ? 1u : 0u;
-    });
+    uint32_t cnt = 0u;
+    sv.for_each_group([&](int i) { cnt += take(i) ? 1u : 0u; });
     const uint32_t incl = wave_inclusive_sum(cnt);
-    uint32_t tpos = 64u * w;
-    if (!by_icut) {
-        const uint32_t tincl = wave_inclusive_sum(tcnt);
-        tpos += tincl - tcnt;
-        if (lane == 63u) wtot[kWaves + w] = tincl;
-        const uint32_t tspare = (uint32_t)(64 * kWaves) + lane;
-        const uint32_t tend = 64u * w + 64u;
-        sv.for_each_group([&](int i) {
-            bool tie;
-            look(i, tie);
-            tw[(tie & (tpos < tend)) ? tpos : tspare] = sv.idx[i];
-            tpos += tie ? 1u : 0u;
-        });
-    }
     if (lane == 63u) wtot[w] = incl;
     B::sync();
-    uint32_t base = incl - cnt, total = 0u;
+    uint32_t base = incl - cnt;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        const uint32_t c = wtot[i];
-        base += (uint32_t)i < w ? c : 0u;
-        total += c;
-    }
+    for (int i = 0; i < kWaves; ++i) base += (uint32_t)i < w ? wtot[i] : 0u;
     const uint32_t spare = (uint32_t)TOPK_MAX_K + lane;
     sv.for_each_group([&](int i) {
-        bool tie;
-        const bool t = look(i, tie);
+        const bool t = take(i);
         const int32_t o = map(t ? sv.idx[i] : 0u);
         lst[(t & (base < m)) ? base : spare] = (uint32_t)o;
         base += t ? 1u : 0u;
     });
-    if (!by_icut && w == 0u) {
-        // lane l takes the l-th gathered tie, wave region by wave region
-        uint32_t v = 0xFFFFFFFFu, first = 0u;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-            const uint32_t c = min(wtot[kWaves + i], 64u);
-            if (lane >= first && lane < first + c) v = tw[i * 64 + (lane - first)];
-            first += c;
-        }
-        uint32_t V = 0u;
-        for (int bit = idx_bits - 1; bit >= 0; --bit) {
-            const uint32_t c = V | (1u << bit);
-            if ((uint32_t)__popcll(__ballot(v < c)) < sel.need) V = c;
-        }
-        const bool chosen = v <= V;  // positions are below 2^idx_bits, so the unused lanes stay out
-        const uint32_t slot = total + lanes_below(__ballot(chosen));
-        const int32_t o = map(chosen ? v : 0u);
-        lst[(chosen & (slot < m)) ? slot : spare] = (uint32_t)o;
-    }
     B::sync();
     constexpr int kPer = (TOPK_MAX_K + B::kSize - 1) / B::kSize;  // list words per thread, all read at once
     uint32_t o[kPer];
@@ -831,11 +830,13 @@ __device__ __forceinline__ void emit_slots(const RegPairs<N>& sv, SurvSel sel, u
 // launch 3: the exact top m of each row
 __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p) {
     using B = BlockScope<kFinThreads>;
-    __shared__ uint32_t ews[emit_words<kFinThreads / 64>()];  // the emission's list and tie regions
+    __shared__ __align__(16) uint32_t ews[kListWords];  // the emission's list; first the members a selection ranks
+    __shared__ uint32_t mcount;
+    __shared__ uint2 pick;
     __shared__ uint32_t hist[kBins + 64];
     __shared__ uint32_t found[3];
     __shared__ uint32_t emitted;
-    __shared__ uint32_t wtot[2 * (kFinThreads / 64)];
+    __shared__ uint32_t wtot[kFinThreads / 64];
     __shared__ uint32_t smax;  // the largest survivor key
     const int64_t b = blockIdx.x;
     const SplitHead head = p.head[b];
@@ -844,6 +845,7 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
     if (threadIdx.x == 0) {
         emitted = 0u;
         smax = 0u;
+        mcount = 0u;
     }
     const int64_t L = split_row_len(p, b);
     const uint32_t m = (uint32_t)(L < p.k ? L : p.k);
@@ -868,9 +870,9 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
             const uint32_t e = (uint32_t)(i * kFinThreads) + threadIdx.x;
-            uint2 v = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+            uint2 v = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);  // key 0: the NaN pattern all ones
             if (e < n) v = g[e];
-            sv.bits[i] = v.x;
+            sv.key[i] = order_key(__uint_as_float(v.x));
             sv.idx[i] = v.y;
         }
         uint32_t hmax = 0u;
@@ -878,12 +880,13 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
         hmax = wave_max(hmax);
         if (lane_id() == 0) atomicMax(&smax, hmax);
         B::sync();
-        const SurvSel s = short_select<F32Elem, B>(lds, sv, m, n, head.T, smax, bits_for(L));
+        const Selection s = short_select<F32Elem, B>(lds, sv, m, n, head.T, smax, bits_for(L),
+                                                     reinterpret_cast<uint2*>(ews), &mcount, &pick);
         int32_t* row = p.out + b * (int64_t)p.k;
         if (p.page_table == nullptr)
-            emit_slots<B>(sv, s, m, row, NoMap{}, bits_for(L), wtot, ews);
+            emit_slots<B>(sv, s, m, row, NoMap{}, wtot, ews);
         else
-            emit_slots<B>(sv, s, m, row, global_map(p, b), bits_for(L), wtot, ews);
+            emit_slots<B>(sv, s, m, row, global_map(p, b), wtot, ews);
     }
     if (threadIdx.x == 0) split_stats(p, b, code, head.kind == kKindFull ? (uint32_t)L : n);
 }
@@ -911,7 +914,9 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     __shared__ uint32_t found[3];
     __shared__ uint32_t count;
     __shared__ uint32_t emitted;
-    __shared__ uint32_t wtot[2 * (kThreads / 64)];
+    __shared__ uint32_t wtot[kThreads / 64];
+    __shared__ uint32_t mcount;
+    __shared__ uint2 pick;
     const int64_t b = blockIdx.x;
     const int64_t L = split_row_len(p, b);
     const uint32_t m = (uint32_t)(L < p.k ? L : p.k);
@@ -925,6 +930,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     if (threadIdx.x == 0) {
         count = 0u;
         emitted = 0u;
+        mcount = 0u;
     }
     B::sync();
     const SelectLds lds{hist, found};
@@ -1088,10 +1094,10 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         for (int i = 0; i < kSlots; ++i) {
             const uint32_t e = (uint32_t)(i * kThreads) + threadIdx.x;
             const uint2 v = buf[e];
-            sv.bits[i] = e < n ? v.x : 0xFFFFFFFFu;
+            sv.key[i] = e < n ? order_key(__uint_as_float(v.x)) : 0u;
             sv.idx[i] = e < n ? v.y : 0xFFFFFFFFu;
         }
-        const SurvSel s = short_select<E, B>(lds, sv, m, n, T, cut.hi, bits_for(L));
+        const Selection s = short_select<E, B>(lds, sv, m, n, T, cut.hi, bits_for(L), buf, &mcount, &pick);
         if (stage) {  // the selection has left the histogram (the emission syncs before reading)
 #pragma unroll
             for (int i = 0; i < kPg; ++i) {
@@ -1100,8 +1106,8 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
             }
         }
         int32_t* row = p.out + b * (int64_t)p.k;
-        uint32_t* tw = reinterpret_cast<uint32_t*>(buf);
-        static_assert(emit_words<kThreads / 64>() <= 2 * (kShortCap + 64), "the emission fits the buffer");
+        uint32_t* lst = reinterpret_cast<uint32_t*>(buf);
+        static_assert(kListWords <= 2 * (kShortCap + 64), "the emission's list fits the buffer");
         // Without a page table the staged map is the identity: with l = 31,
         // every position reads hist[0], which the selection left at 0. (Two
         // variants, not three: with a third, the compiler keeps the survivor
@@ -1110,9 +1116,9 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
             emit_slots<B>(sv, s, m, row,
                           LdsShiftMap{(LdsI32)reinterpret_cast<const int32_t*>(hist),
                                       pages == nullptr ? 31u : (uint32_t)(31 - __clz(p.page_size))},
-                          bits_for(L), wtot, tw);
+                          wtot, lst);
         else
-            emit_slots<B>(sv, s, m, row, global_map(p, b), bits_for(L), wtot, tw);
+            emit_slots<B>(sv, s, m, row, global_map(p, b), wtot, lst);
     }
     if (threadIdx.x == 0) split_stats(p, b, code, n);
 }

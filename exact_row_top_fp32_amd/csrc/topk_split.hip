@@ -264,11 +264,15 @@ struct F32Elem {
         return SurvivorBound{t, t};
     }
     template <bool kPos>
-    __device__ static bool pass(const Vec& v, int j, SurvivorBound b, uint32_t& out_bits) {
+    __device__ static bool pass(const Vec& v, int j, SurvivorBound b) {
         const uint32_t x = __float_as_uint(v[j]);
-        out_bits = x;
         return kPos ? (int32_t)x >= (int32_t)b.t : x <= b.t;
     }
+    // the 32-bit word of a load holding element j, the fp32 bits of the
+    // score at position i held in such a word, and a word holding bits there
+    __device__ static uint32_t word(const Vec& v, int j) { return __float_as_uint(v[j]); }
+    __device__ static uint32_t word_bits(uint32_t w, uint32_t) { return w; }
+    __device__ static uint32_t bits_word(uint32_t bits, uint32_t) { return bits; }
 };
 struct Bf16Elem {
     typedef u4 Vec;
@@ -297,12 +301,17 @@ struct Bf16Elem {
         return SurvivorBound{t, t >> 16};
     }
     template <bool kPos>
-    __device__ static bool pass(const Vec& v, int j, SurvivorBound b, uint32_t& out_bits) {
+    __device__ static bool pass(const Vec& v, int j, SurvivorBound b) {
         const uint32_t w = v[j >> 1];
         const uint32_t h = (j & 1) ? (w >> 16) : (w & 0xFFFFu);
-        out_bits = (j & 1) ? (w & 0xFFFF0000u) : (w << 16);
         return kPos ? (int32_t)(int16_t)h >= (int32_t)b.th : h <= b.th;
     }
+    // Element j of a load is half j & 1 of word j >> 1, and positions keep
+    // that parity (a load starts at a multiple of 8): a survivor is kept as
+    // its whole word and its position.
+    __device__ static uint32_t word(const Vec& v, int j) { return v[j >> 1]; }
+    __device__ static uint32_t word_bits(uint32_t w, uint32_t i) { return (i & 1u) ? (w & 0xFFFF0000u) : (w << 16); }
+    __device__ static uint32_t bits_word(uint32_t bits, uint32_t i) { return (i & 1u) ? bits : bits >> 16; }
 };
 
 template <class E>
@@ -400,6 +409,13 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
     const typename E::Vec* rv = reinterpret_cast<const typename E::Vec*>(row);
     // the row's first load lies `lead` loads into its 128-byte line
     const int64_t lead = (int64_t)((reinterpret_cast<uintptr_t>(row) & 127u) >> 4);
+    // floor(r * span / (runs - 1)) = r quo + floor(r rem / (runs - 1)), the
+    // last term taken in fp32 as floor((r rem + 1/2) / (runs - 1)): r rem is
+    // below 2^12 and (r rem + 1/2) / (runs - 1) lies at least 1/126 from
+    // every integer, far more than the rounding error of the product
+    const int64_t quo = runs == kRuns ? span / (kRuns - 1) : span / (runs - 1);  // uniform; a constant divisor mostly
+    const uint32_t rem = (uint32_t)(span - quo * (runs - 1));
+    const float inv = 1.0f / (float)(runs - 1);
     typename E::Vec x[kPer];
 #pragma unroll
     for (int h = 0; h < kPer; ++h) {
@@ -408,7 +424,8 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
         // run r starts near floor(r * span / (runs - 1)), moved down to the
         // start of a 128-byte line (a run of 64 scores then covers whole
         // lines only; the first run stays at 0 when that would go below it)
-        int64_t start = ((int64_t)r * span / (runs - 1)) / E::kPerVec;
+        const uint32_t frac = (uint32_t)(((float)((uint32_t)r * rem) + 0.5f) * inv);
+        int64_t start = ((int64_t)r * quo + frac) / E::kPerVec;
         start = (start + lead) / kLineVecs * kLineVecs - lead;
         start = start < 0 ? 0 : start;
         if (t < nsv) x[h] = rv[start + t % kVecPerRun];
@@ -609,20 +626,6 @@ __global__ __launch_bounds__(kThreads) void split_stream_kernel(SplitParams p) {
     stream_piece(p, b, split_row_len(p, b), h->T, piece, h, p.surv + b * kSplitCapacity, (uint32_t)p.capacity);
 }
 
-// The first pass of a survivor selection: keys up to hi in bins of
-// (key >> shift - base) >> sh, base aligned to 2^sh, so that bin d holds
-// exactly the keys up to hi whose top bits are (base >> sh) + d; keys above
-// hi in the top bin.
-template <int kShift>
-struct AboveBinView {
-    uint32_t base, hi;
-    int sh;
-    __device__ bool operator()(uint32_t key, uint32_t, uint32_t& v) const {
-        const uint32_t x = key >> kShift;
-        v = x > hi ? (uint32_t)(kBins - 1) : (x - base) >> sh;
-        return true;
-    }
-};
 // key >> shift, for the keys in [lo, hi]
 template <int kShift>
 struct ShiftedRangeView {
@@ -640,15 +643,19 @@ struct ShiftedRangeView {
 // writes without branches. Then one wave holds a member per lane and ranks
 // each by key, largest first, and position, lowest first, against every
 // other (read across lanes); the member of rank need - 1 gives the cutoff
-// key and the last position taken at it. This replaces a radix pass over
-// the positions and any ranking of ties in the emission.
+// key and the last position taken at it. When the members share one key,
+// that position is found bit by bit from counts over the wave instead. This
+// replaces a radix pass over the positions and any ranking of ties in the
+// emission.
 template <class B, int N, int kShift>
 __device__ __forceinline__ Selection rank_members(const RegPairs<N>& sv, uint32_t lo_x, uint32_t hi_x,
-                                                  uint32_t need, uint2* mem, uint32_t* mcount, uint2* pick) {
+                                                  uint32_t need, int idx_bits, uint2* mem, uint32_t* mcount,
+                                                  uint2* pick) {
+    // lo_x is at least the cutoff's shifted key, above the 0 of an empty slot
+    const uint32_t width = hi_x - lo_x;
     auto member = [&](int i, uint32_t& key) {
         key = sv.key[i];
-        const uint32_t x = key >> kShift;
-        return (sv.idx[i] != 0xFFFFFFFFu) & (x >= lo_x) & (x <= hi_x);
+        return (key >> kShift) - lo_x <= width;
     };
     uint32_t cnt = 0u;
     sv.for_each_group([&](int i) {
@@ -673,18 +680,26 @@ __device__ __forceinline__ Selection rank_members(const RegPairs<N>& sv, uint32_
     if (B::first_wave()) {
         const uint32_t ne = __builtin_amdgcn_readfirstlane(min(*mcount, (uint32_t)kMaxCand)), lane = lane_id();
         const uint2 me = lane < ne ? mem[lane] : make_uint2(0u, 0xFFFFFFFFu);
-        uint32_t rank = 0u;
-        if (lo_x == hi_x) {  // one key (a shifted key fixes the full one): by position alone
-            for (uint32_t j = 0; j < ne; ++j)
-                rank += (uint32_t)__builtin_amdgcn_readlane((int)me.y, (int)j) < me.y ? 1u : 0u;
+        if (lo_x == hi_x) {
+            // One key (a shifted key fixes the full one): the need-th lowest
+            // position P, built from the top bit down: a bit stays 0 when at
+            // least need members lie below the value with it set (the
+            // positions below 2^idx_bits; padding lanes hold 0xFFFFFFFF).
+            uint32_t at = 0u;
+            for (int bit = idx_bits - 1; bit >= 0; --bit) {
+                const uint32_t t = at | (1u << bit);
+                if ((uint32_t)__builtin_popcountll(__ballot(me.y < t)) < need) at = t;
+            }
+            if (lane == 0u) *pick = make_uint2(me.x, at);
         } else {
+            uint32_t rank = 0u;
             for (uint32_t j = 0; j < ne; ++j) {
                 const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)me.x, (int)j);
                 const uint32_t op = (uint32_t)__builtin_amdgcn_readlane((int)me.y, (int)j);
                 rank += ((ok > me.x) | ((ok == me.x) & (op < me.y))) ? 1u : 0u;
             }
+            if ((lane < ne) & (rank == need - 1u)) *pick = me;
         }
-        if ((lane < ne) & (rank == need - 1u)) *pick = me;
     }
     B::sync();
     const uint2 w = *pick;
@@ -704,19 +719,32 @@ __device__ __forceinline__ Selection rank_members(const RegPairs<N>& sv, uint32_
 // 64 survivors is ranked directly (rank_members) instead of by further radix
 // passes. `mem` (64 + 64 entries), `mcount` and `pick` are rank_members' LDS.
 template <class E, class B, int N>
-__device__ Selection short_select(SelectLds lds, const RegPairs<N>& src, uint32_t m, uint32_t n, uint32_t T,
-                                  uint32_t hi_key, int idx_bits, uint2* mem, uint32_t* mcount, uint2* pick) {
+__device__ __forceinline__ Selection short_select(SelectLds lds, const RegPairs<N>& src, uint32_t m, uint32_t T,
+                                                  uint32_t hi_key, int idx_bits, uint2* mem, uint32_t* mcount,
+                                                  uint2* pick) {
     constexpr int kShift = E::kKeyShift;
     constexpr uint32_t kTop = 0xFFFFFFFFu >> kShift;
     const uint32_t lo = T >> kShift, hi = max(hi_key >> kShift, lo);
     const int sh = bin_shift(hi - lo);
     const uint32_t base = lo & ~((1u << sh) - 1u);  // (hi - base) >> sh <= kBins - 2
-    const Cut c1 = radix_select_slots<B>(lds, src, AboveBinView<kShift>{base, hi, sh}, m, 0u, kDigitBits, n);
+    // The first pass: keys x = key >> kShift up to hi in bins (x - base) >> sh
+    // (base aligned to 2^sh, so bin d holds exactly the keys up to hi whose
+    // top bits are (base >> sh) + d), keys above hi in the top bin, an empty
+    // slot (key 0) in its lane's sink bin.
+    const uint32_t sink = (uint32_t)kBins + lane_id();
+    src.for_each_group([&](int i) {
+        const uint32_t key = src.key[i], x = key >> kShift;
+        const uint32_t d = x > hi ? (uint32_t)(kBins - 1) : (x - base) >> sh;
+        atomicAdd(&lds.hist[key != 0u ? d : sink], 1u);
+    });
+    B::sync();
+    const Found f1 = find_rank_bin<B>(lds, m);
+    const Cut c1{f1.digit, m - f1.above, f1.count, false};
     Cut c;
     if (c1.value == (uint32_t)(kBins - 1)) {  // the cutoff is above hi (so hi < kTop)
         if (c1.need == c1.equal) return at_least((hi + 1u) << kShift);
         if (c1.equal <= (uint32_t)kMaxCand)
-            return rank_members<B, N, kShift>(src, hi + 1u, kTop, c1.need, mem, mcount, pick);
+            return rank_members<B, N, kShift>(src, hi + 1u, kTop, c1.need, idx_bits, mem, mcount, pick);
         c = radix_select_slots<B>(lds, src, ShiftedRangeView<kShift>{hi + 1u, kTop}, c1.need, 0u, 32 - kShift,
                                   c1.equal);
         if (c.range) return at_least(c.value << kShift);
@@ -727,7 +755,7 @@ __device__ Selection short_select(SelectLds lds, const RegPairs<N>& src, uint32_
         // bits were counted in the top bin, so they stay out
         const uint32_t bin_hi = min(edge + ((1u << sh) - 1u), hi);
         if (c1.equal <= (uint32_t)kMaxCand)
-            return rank_members<B, N, kShift>(src, edge, bin_hi, c1.need, mem, mcount, pick);
+            return rank_members<B, N, kShift>(src, edge, bin_hi, c1.need, idx_bits, mem, mcount, pick);
         c = Cut{edge, c1.need, c1.equal, false};
         if (sh > 0) {
             c = radix_select_slots<B>(lds, src, ShiftedRangeView<kShift>{edge, hi}, c1.need, edge, sh, c1.equal);
@@ -736,7 +764,8 @@ __device__ Selection short_select(SelectLds lds, const RegPairs<N>& src, uint32_
     }
     const uint32_t kth = E::full_key(c.value);
     if (c.need >= c.equal) return Selection{kth, INT32_MAX};
-    if (c.equal <= (uint32_t)kMaxCand) return rank_members<B, N, kShift>(src, c.value, c.value, c.need, mem, mcount, pick);
+    if (c.equal <= (uint32_t)kMaxCand)
+        return rank_members<B, N, kShift>(src, c.value, c.value, c.need, idx_bits, mem, mcount, pick);
     // the need-th largest inverted index among the ties (select_top's way)
     const uint32_t iprefix = idx_bits >= 32 ? 0u : (0xFFFFFFFFu << idx_bits);
     const Cut t = radix_select_slots<B>(lds, src, TieIndexView{kth}, c.need, iprefix, idx_bits, c.equal);
@@ -867,20 +896,19 @@ __global__ __launch_bounds__(kFinThreads) void split_finish_kernel(SplitParams p
         const uint2* g = p.surv + b * kSplitCapacity;
         RegPairs<kSlots> sv;
         sv.nslot = (int)((n + kFinThreads - 1) / kFinThreads);
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
+        sv.for_each_group([&](int i) {  // slots of the groups past nslot are never read
             const uint32_t e = (uint32_t)(i * kFinThreads) + threadIdx.x;
             uint2 v = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);  // key 0: the NaN pattern all ones
             if (e < n) v = g[e];
             sv.key[i] = order_key(__uint_as_float(v.x));
             sv.idx[i] = v.y;
-        }
+        });
         uint32_t hmax = 0u;
         sv.for_each_slot([&](uint32_t key, uint32_t, bool valid) { hmax = max(hmax, valid ? key : 0u); });
         hmax = wave_max(hmax);
         if (lane_id() == 0) atomicMax(&smax, hmax);
         B::sync();
-        const Selection s = short_select<F32Elem, B>(lds, sv, m, n, head.T, smax, bits_for(L),
+        const Selection s = short_select<F32Elem, B>(lds, sv, m, head.T, smax, bits_for(L),
                                                      reinterpret_cast<uint2*>(ews), &mcount, &pick);
         int32_t* row = p.out + b * (int64_t)p.k;
         if (p.page_table == nullptr)
@@ -907,8 +935,9 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     constexpr int64_t kR = (int64_t)kThreads * kU;  // loads per workgroup round
     using B = BlockScope<kThreads>;
     typedef typename E::Vec Vec;
-    // the survivors (one spare entry per lane past them), later the waves'
-    // tie regions
+    // the survivors, as two arrays of words: the word of the load that held
+    // each (words[]) and its position (words[kShortCap + ...]); later the
+    // selection's and the emission's lists
     __shared__ uint2 buf[kShortCap + 64];
     __shared__ uint32_t hist[kBins + 64];
     __shared__ uint32_t found[3];
@@ -960,11 +989,21 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     // which no score test passes, so the filter needs no bounds. With a fixed
     // number of loads issued after the sample's, the sample can be used once
     // its own loads are in, these still in flight.
+    // A round wholly inside the row (uniform) takes one scalar base and
+    // the lane's offset for all its loads.
     auto load = [&](int64_t base, Vec (&x)[kU]) {
+        if (base + kR <= nvec) {
+            typedef __attribute__((address_space(1))) const char* GBytes;
+            const GBytes r0 = (GBytes)(rv + base);
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int64_t g = base + u * kThreads + threadIdx.x;
-            x[u] = __builtin_nontemporal_load(g < nvec ? rv + g : pad);
+            for (int u = 0; u < kU; ++u)
+                x[u] = __builtin_nontemporal_load((GVec)(r0 + (uint32_t)((u * kThreads + threadIdx.x) * sizeof(Vec))));
+        } else {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t g = base + u * kThreads + threadIdx.x;
+                x[u] = __builtin_nontemporal_load(g < nvec ? rv + g : pad);
+            }
         }
     };
     Vec xa[kU], xc[kU];
@@ -973,7 +1012,7 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     // fails the survivor test, on the other lanes)
     const int64_t tail0 = nvec * E::kPerVec;
     typedef __attribute__((address_space(1))) const typename E::Scalar* GScalar;
-    uint32_t tbits = 0xFFFFFFFFu;
+    uint32_t tbits = 0xFFFFFFFFu;  // the fp32 bits of the lane's tail score
     auto first_loads = [&](bool) {
         load(0, xa);
         load(kR, xc);
@@ -992,19 +1031,16 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     // One round: each lane counts its survivors, one LDS reservation per wave
     // places them (a wave that would pass the capacity writes nothing; the
     // count still grows, so the row then takes the full-row selection), and
-    // each lane writes its survivors to consecutive slots. Every lane writes
-    // for every score, a failing one to the lane's spare entry, so that the
-    // writes need no branches.
+    // each lane writes its survivors to consecutive slots, only the lanes
+    // whose score passes taking part in a write.
+    uint32_t* const sw = reinterpret_cast<uint32_t*>(buf);
     auto filter = [&](auto pos_tag, const Vec (&x)[kU], int64_t base) {
         constexpr bool kPos = decltype(pos_tag)::value;
         uint32_t cnt = 0u;
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
 #pragma unroll
-            for (int j = 0; j < E::kPerVec; ++j) {
-                uint32_t bits;
-                cnt += E::template pass<kPos>(x[u], j, sb, bits) ? 1u : 0u;
-            }
+            for (int j = 0; j < E::kPerVec; ++j) cnt += E::template pass<kPos>(x[u], j, sb) ? 1u : 0u;
         }
         const uint32_t incl = wave_inclusive_sum(cnt);
         const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
@@ -1013,10 +1049,10 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         if (lane_id() == 0) wbase = atomicAdd(&count, total);
         wbase = __builtin_amdgcn_readfirstlane(wbase);
         if (wbase + total > cap) return;
-        // byte offsets into the buffer: the lane's next slot and its spare
-        uint32_t slot = (wbase + incl - cnt) * (uint32_t)sizeof(uint2);
-        const uint32_t spare = ((uint32_t)kShortCap + lane_id()) * (uint32_t)sizeof(uint2);
-        char* const bytes = reinterpret_cast<char*>(buf);
+        // byte offset of the lane's next slot in the word array (positions
+        // lie kShortCap words further on)
+        uint32_t slot = (wbase + incl - cnt) * (uint32_t)sizeof(uint32_t);
+        char* const bytes = reinterpret_cast<char*>(sw);
         const uint32_t p0 = (uint32_t)(E::kPerVec * (base + threadIdx.x));
         // The tests run again here rather than keep 32 results per lane live
         // across the reservation: the bounds are taken through wbase >> 31,
@@ -1027,11 +1063,12 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         for (int u = 0; u < kU; ++u) {
 #pragma unroll
             for (int j = 0; j < E::kPerVec; ++j) {
-                uint32_t bits;
-                const bool ok = E::template pass<kPos>(x[u], j, sb2, bits);
-                *reinterpret_cast<uint2*>(bytes + (ok ? slot : spare)) =
-                    make_uint2(bits, p0 + (uint32_t)(E::kPerVec * kThreads * u + j));
-                slot += ok ? (uint32_t)sizeof(uint2) : 0u;
+                if (__builtin_expect(E::template pass<kPos>(x[u], j, sb2), 1)) {  // some lane passes
+                    *reinterpret_cast<uint32_t*>(bytes + slot) = E::word(x[u], j);
+                    *reinterpret_cast<uint32_t*>(bytes + slot + kShortCap * sizeof(uint32_t)) =
+                        p0 + (uint32_t)(E::kPerVec * kThreads * u + j);
+                    slot += (uint32_t)sizeof(uint32_t);
+                }
             }
         }
     };
@@ -1054,7 +1091,11 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     if (tail0 < L && wave_id() == 0) {
         const bool hit = pos ? (int32_t)tbits >= (int32_t)sb.t : tbits <= sb.t;  // exact widened bits
         const uint32_t slot = wave_reserve_count(&count, hit ? 1u : 0u);
-        if (hit && slot < cap) buf[slot] = make_uint2(tbits, (uint32_t)(tail0 + threadIdx.x));
+        if (hit && slot < cap) {
+            const uint32_t i = (uint32_t)(tail0 + threadIdx.x);
+            sw[slot] = E::bits_word(tbits, i);
+            sw[kShortCap + slot] = i;
+        }
     }
     B::sync();
     const uint32_t n = count;
@@ -1079,30 +1120,33 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         if (stage) {
 #pragma unroll
             for (int i = 0; i < kPg; ++i) {
-                const uint32_t t = (uint32_t)(i * kThreads) + threadIdx.x;
-                if (t < npg) pg[i] = pages[t];
+                if ((uint32_t)(i * kThreads) < npg) {  // uniform
+                    const uint32_t t = (uint32_t)(i * kThreads) + threadIdx.x;
+                    if (t < npg) pg[i] = pages[t];
+                }
             }
         }
         // the survivors into registers, every read in flight at once (the LDS
         // buffer then holds the tie regions; the selection's first barrier
         // orders the two uses)
         constexpr int kSlots = (kShortCap + kThreads - 1) / kThreads;
-        static_assert(kSlots * kThreads <= kShortCap + 64, "every slot reads inside the buffer");
+        static_assert(kSlots * kThreads <= kShortCap, "every slot reads inside the word array");
         RegPairs<kSlots> sv;
         sv.nslot = (int)((n + kThreads - 1) / kThreads);
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
+        sv.for_each_group([&](int i) {  // slots of the groups past nslot are never read
             const uint32_t e = (uint32_t)(i * kThreads) + threadIdx.x;
-            const uint2 v = buf[e];
-            sv.key[i] = e < n ? order_key(__uint_as_float(v.x)) : 0u;
-            sv.idx[i] = e < n ? v.y : 0xFFFFFFFFu;
-        }
-        const Selection s = short_select<E, B>(lds, sv, m, n, T, cut.hi, bits_for(L), buf, &mcount, &pick);
+            const uint32_t w = sw[e], at = sw[kShortCap + e];
+            sv.key[i] = e < n ? order_key(__uint_as_float(E::word_bits(w, at))) : 0u;
+            sv.idx[i] = e < n ? at : 0xFFFFFFFFu;
+        });
+        const Selection s = short_select<E, B>(lds, sv, m, T, cut.hi, bits_for(L), buf, &mcount, &pick);
         if (stage) {  // the selection has left the histogram (the emission syncs before reading)
 #pragma unroll
             for (int i = 0; i < kPg; ++i) {
-                const uint32_t t = (uint32_t)(i * kThreads) + threadIdx.x;
-                if (t < npg) reinterpret_cast<int32_t*>(hist)[t] = pg[i];
+                if ((uint32_t)(i * kThreads) < npg) {  // uniform
+                    const uint32_t t = (uint32_t)(i * kThreads) + threadIdx.x;
+                    if (t < npg) reinterpret_cast<int32_t*>(hist)[t] = pg[i];
+                }
             }
         }
         int32_t* row = p.out + b * (int64_t)p.k;

@@ -152,18 +152,31 @@ struct Found {
     uint32_t count;  // elements in that bin
 };
 
+// A lane's q-th 16-byte read of its own run of 32 words, the runs of all
+// lanes 128 bytes apart: the lanes take the run's 8 pieces in rotated orders
+// (q + lane + lane / 8, mod 8), so that the lanes of one read touch distinct
+// LDS banks, 8 lanes at a time over 32 banks or 16 at a time over 64 (in
+// plain order every lane would touch the same four banks).
+__device__ __forceinline__ int run_piece(int q, uint32_t lane) {
+    return (int)(((uint32_t)q + lane + (lane >> 3)) & 7u);
+}
+
 // One wave: the bin of the rank-th element from the top of a 2048-bin
 // histogram (a wave prefix sum over 32-bin groups, lane 0 holding the top
 // group, then one over the chosen group's bins). Every lane gets the result;
-// the histogram is left as it is. 1 <= rank <= histogram total.
+// the histogram is left as it is. 1 <= rank <= histogram total. kSpread:
+// the group reads in rotated order (run_piece), free of bank conflicts at
+// the cost of a few registers.
+template <bool kSpread = false>
 __device__ __forceinline__ Found wave_locate(const uint32_t* hist, uint32_t rank) {
+    static_assert(kBinsPerLane == 32, "a run of 8 16-byte pieces per lane");
     const uint32_t lane = lane_id();
     const uint32_t base = kBins - kBinsPerLane * (lane + 1);
     const uint4* h4 = reinterpret_cast<const uint4*>(hist + base);
     uint32_t s = 0;
 #pragma unroll
     for (int q = 0; q < kBinsPerLane / 4; ++q) {
-        const uint4 v = h4[q];
+        const uint4 v = h4[kSpread ? run_piece(q, lane) : q];
         s += v.x + v.y + v.z + v.w;
     }
     const uint32_t incl = wave_inclusive_sum(s);
@@ -188,15 +201,17 @@ __device__ __forceinline__ Found wave_locate(const uint32_t* hist, uint32_t rank
 
 // After the histogram atomics of a pass and a sync: the scope's first wave
 // locates the bin of the rank-th element from the top, zeroes the histogram
-// for the next pass and publishes the bin to the scope.
-template <class S>
+// for the next pass and publishes the bin to the scope. kSpread as for
+// wave_locate.
+template <class S, bool kSpread = false>
 __device__ __forceinline__ Found find_rank_bin(SelectLds lds, uint32_t rank) {
     if (S::first_wave()) {
-        const Found f = wave_locate(lds.hist, rank);
+        const Found f = wave_locate<kSpread>(lds.hist, rank);
         const uint32_t lane = lane_id();
         uint4* h4 = reinterpret_cast<uint4*>(lds.hist + kBins - kBinsPerLane * (lane + 1));
 #pragma unroll
-        for (int q = 0; q < kBinsPerLane / 4; ++q) h4[q] = make_uint4(0u, 0u, 0u, 0u);
+        for (int q = 0; q < kBinsPerLane / 4; ++q)
+            h4[kSpread ? run_piece(q, lane) : q] = make_uint4(0u, 0u, 0u, 0u);
         if (lane == 0) {
             lds.found[0] = f.digit;
             lds.found[1] = f.above;

@@ -213,7 +213,7 @@ __device__ __forceinline__ Cut radix_select_slots(SelectLds lds, const Src& src,
             atomicAdd(&lds.hist[in ? (v >> shift) & dmask : sink], 1u);
         });
         S::sync();
-        const Found f = find_rank_bin<S>(lds, rank);
+        const Found f = find_rank_bin<S, true>(lds, rank);
         rank -= f.above;
         prefix = want | (f.digit << shift);
         nbits = shift;
@@ -435,52 +435,68 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
     const float mu = (float)m * (float)n / (float)L;
     const float wantf = ceilf(mu + 6.0f * sqrtf(mu) + 4.0f);
     const uint32_t want = wantf < (float)n ? (uint32_t)wantf : 0u;  // 0: keep every score
-    // Each lane also keeps its kQ largest keys (and so its largest). With
-    // q = ceil(want / kThreads) <= kQ, the smallest of the lanes' q-th
-    // largest keys, lo, has at least want keys at or above it (a lane with
-    // fewer than q keys gives lo = 0).
+    // Each lane also keeps its q largest keys (and so its largest), q =
+    // ceil(want / kThreads) when that is at most kQ. The smallest of the
+    // lanes' q-th largest keys, lo, has at least want keys at or above it (a
+    // lane with fewer than q keys gives lo = 0).
     constexpr int kQ = 4;
-    uint32_t top[kQ] = {0u, 0u, 0u, 0u};
-    uint32_t fin = 0u;  // the lane's largest key below +inf's
+    const uint32_t q = (want + kThreads - 1) / kThreads;
+    const bool one_pass = want > 0u && q <= (uint32_t)kQ;  // uniform
+    uint32_t lane_lo = 0u;  // the lane's q-th largest key
+    uint32_t fin = 0u;      // the lane's largest key below +inf's
     uint32_t skey[kPer * E::kPerVec];
     const RegKeys<kPer, E::kPerVec> keys{skey, nsv};
 #pragma unroll
     for (int h = 0; h < kPer; ++h) {
-        const int t = h * kThreads + (int)threadIdx.x;
 #pragma unroll
         for (int j = 0; j < E::kPerVec; ++j) skey[h * E::kPerVec + j] = elem_key<E>(E::bits(x[h], j));
-        if (t < nsv) {
+    }
+    // the lane's K largest keys by insertion, K = q rounded up to 1, 2 or kQ
+    auto lane_tops = [&](auto k_tag) {
+        constexpr int K = decltype(k_tag)::value;
+        uint32_t top[K];
 #pragma unroll
-            for (int j = 0; j < E::kPerVec; ++j) {
-                uint32_t key = skey[h * E::kPerVec + j];
-                fin = max(fin, key < kInfKey ? key : 0u);
+        for (int i = 0; i < K; ++i) top[i] = 0u;
 #pragma unroll
-                for (int i = 0; i < kQ; ++i) {
-                    const uint32_t hi = max(top[i], key);
-                    key = min(top[i], key);
-                    top[i] = hi;
+        for (int h = 0; h < kPer; ++h) {
+            if (h * kThreads + (int)threadIdx.x < nsv) {
+#pragma unroll
+                for (int j = 0; j < E::kPerVec; ++j) {
+                    uint32_t key = skey[h * E::kPerVec + j];
+                    fin = max(fin, key < kInfKey ? key : 0u);
+#pragma unroll
+                    for (int i = 0; i < K; ++i) {
+                        const uint32_t hi = max(top[i], key);
+                        key = min(top[i], key);
+                        top[i] = hi;
+                    }
                 }
             }
         }
-    }
-    const uint32_t q = (want + kThreads - 1) / kThreads;
-    const bool one_pass = want > 0u && q <= (uint32_t)kQ;  // uniform
-    __shared__ uint32_t s_lo, s_hi;
-    if (threadIdx.x == 0) {
-        s_lo = 0xFFFFFFFFu;
-        s_hi = 0u;
-    }
-    B::sync();
-    uint32_t lane_lo = top[0];
+        lane_lo = top[0];
 #pragma unroll
-    for (int i = 1; i < kQ; ++i) lane_lo = (uint32_t)(i + 1) == q ? top[i] : lane_lo;
+        for (int i = 1; i < K; ++i) lane_lo = (uint32_t)(i + 1) == q ? top[i] : lane_lo;
+    };
+    if (q <= 1u)
+        lane_tops(std::integral_constant<int, 1>{});
+    else if (q == 2u)
+        lane_tops(std::integral_constant<int, 2>{});
+    else
+        lane_tops(std::integral_constant<int, kQ>{});
+    // the workgroup's lo and hi from one word per wave
+    __shared__ uint32_t s_lo[kThreads / 64], s_hi[kThreads / 64];
     const uint32_t wlo = wave_min(lane_lo), whi = wave_max(fin);
     if (lane_id() == 0) {
-        atomicMin(&s_lo, wlo);
-        atomicMax(&s_hi, whi);
+        s_lo[wave_id()] = wlo;
+        s_hi[wave_id()] = whi;
     }
     B::sync();
-    const uint32_t shi = s_hi;
+    uint32_t blo = s_lo[0], shi = s_hi[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) {
+        blo = min(blo, s_lo[i]);
+        shi = max(shi, s_hi[i]);
+    }
     if (want == 0u) return Cutoff{0u, shi};
     if (one_pass) {
         // one histogram of the keys in [lo, hi] (hi the largest below +inf),
@@ -488,7 +504,7 @@ __device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_
         // keys above hi in the top bin: T is the lower edge of the bin holding
         // the want-th largest key, or hi + 1 when that key is above hi (bf16
         // keys differ by at least 2^16, so their bins hold one value each)
-        const uint32_t lo = s_lo, hi = max(shi, lo);
+        const uint32_t lo = blo, hi = max(shi, lo);
         const int sh = bin_shift(hi - lo);
         const uint32_t base = lo & ~((1u << sh) - 1u);  // (hi - base) >> sh <= kBins - 2
         const Cut c = radix_select_slots<B>(lds, keys, SampleBinView{lo, hi, base, sh}, want, 0u, kDigitBits, n);
@@ -738,7 +754,7 @@ __device__ __forceinline__ Selection short_select(SelectLds lds, const RegPairs<
         atomicAdd(&lds.hist[key != 0u ? d : sink], 1u);
     });
     B::sync();
-    const Found f1 = find_rank_bin<B>(lds, m);
+    const Found f1 = find_rank_bin<B, true>(lds, m);
     const Cut c1{f1.digit, m - f1.above, f1.count, false};
     Cut c;
     if (c1.value == (uint32_t)(kBins - 1)) {  // the cutoff is above hi (so hi < kTop)
@@ -1152,14 +1168,12 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         int32_t* row = p.out + b * (int64_t)p.k;
         uint32_t* lst = reinterpret_cast<uint32_t*>(buf);
         static_assert(kListWords <= 2 * (kShortCap + 64), "the emission's list fits the buffer");
-        // Without a page table the staged map is the identity: with l = 31,
-        // every position reads hist[0], which the selection left at 0. (Two
-        // variants, not three: with a third, the compiler keeps the survivor
-        // registers in scratch memory.)
-        if (pages == nullptr || stage)
+        if (pages == nullptr)
+            emit_slots<B>(sv, s, m, row, NoMap{}, wtot, lst);
+        else if (stage)
             emit_slots<B>(sv, s, m, row,
                           LdsShiftMap{(LdsI32)reinterpret_cast<const int32_t*>(hist),
-                                      pages == nullptr ? 31u : (uint32_t)(31 - __clz(p.page_size))},
+                                      (uint32_t)(31 - __clz(p.page_size))},
                           wtot, lst);
         else
             emit_slots<B>(sv, s, m, row, global_map(p, b), wtot, lst);

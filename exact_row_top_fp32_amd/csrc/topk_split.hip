@@ -56,7 +56,8 @@ constexpr int kUnroll = 8;                      // 16-byte loads per lane per ro
 constexpr int64_t kRound = kThreads * kUnroll;  // 4-score groups per workgroup round (32 KB)
 constexpr int kRunLen = 64;                     // scores per contiguous sample run
 constexpr int kMaxRuns = 64;                    // sample runs of a split row
-constexpr int kShortRuns = 32;                  // sample runs of a short row
+constexpr int kShortRuns = 32;                  // sample runs of a short row up to kShortLong scores
+constexpr int64_t kShortLong = 16384;           // longer short rows take kMaxRuns runs
 constexpr int kMaxSample = kRunLen * kMaxRuns;  // 4096 keys at most
 constexpr int kMaxPieces = 256;                 // workgroups per row at most
 constexpr int kFinThreads = 1024;               // finisher workgroup: 16 waves
@@ -376,10 +377,13 @@ struct SubBinView {
 // too few keys for that bound, the lowest key of its top 22 bits (two 11-bit
 // digits, at most 2^10 keys below it).
 //
-// The sample has at most kRuns runs: 64 for the split rows, 32 for short
-// rows, where the sample's own work is a larger part of the row's (2048 keys
-// of a 16384-score row leave about 1.4 m survivors for m = 2048, 1.8 m for
-// m = 512, well inside the buffer).
+// The sample has at most kRuns runs: 64 for the split rows and for short rows
+// longer than kShortLong, 32 for the others, where the sample's own work is a
+// larger part of the row's. Over N(0,1) rows, 2048 keys of a 16384-score row
+// leave about 1.4 m survivors for m = 2048 and 1.8 m for m = 512; at 32768
+// scores and m = 2048 they would leave 1.6 m (p99 3680 of the short-row
+// kernel's 3840 entries, before the cutoff moves down to its bin's edge),
+// 4096 keys about 1.4 m.
 //
 // `issue(true)` runs right after the sample's loads are issued (`issue(false)`
 // on the early return of a row too short to sample), so that a caller's own
@@ -1039,7 +1043,8 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     static_assert(kShortCap <= kR * E::kPerVec, "one round covers a row that keeps every score");
     Cutoff cut{0u, 0xFFFFFFFFu};  // a row that keeps every score has no sample
     if (keep_all) first_loads(false);
-    else cut = short_cutoff<E, kShortRuns>(row, L, m, lds, first_loads);
+    else if (L <= kShortLong) cut = short_cutoff<E, kShortRuns>(row, L, m, lds, first_loads);
+    else cut = short_cutoff<E, kMaxRuns>(row, L, m, lds, first_loads);
     // Raising a cutoff below kMinT changes nothing for non-NaN scores (all
     // pass either way) and lets the padded loads fail the survivor test.
     const uint32_t T = max(cut.T, kMinT);

@@ -598,8 +598,9 @@ def sample_positions(L, max_runs, align):
     """Where a sampling path reads a row of length L: runs of 64 scores at
     floor(r (L - 64) / (runs - 1)) rounded down to a multiple of `align`,
     runs = min(L // 128, max_runs). The persistent kernel takes 64 runs on
-    16-byte loads (align 4); the short-row kernel 32 runs on 128-byte lines
-    (align 32 here, where every row starts on a line)."""
+    16-byte loads (align 4); the short-row kernel 32 runs (64 for rows longer
+    than 16384) on 128-byte lines (align 32 here, where every row starts on a
+    line)."""
     runs = min(L // 128, max_runs)
     pos = []
     for r in range(runs):
@@ -624,8 +625,8 @@ def test_sample_that_sees_only_peaks_underflows(topk, W, k):
     assert (W * 4) % 128 == 0
     for b in range(B):
         L = int(lengths[b])
-        pos = np.intersect1d(sample_positions(L, 32 if short else 64, 32 if short else 4),
-                             sample_positions(L, 64, 32))
+        runs = (32 if L <= 16384 else 64) if short else 64
+        pos = np.intersect1d(sample_positions(L, runs, 32 if short else 4), sample_positions(L, 64, 32))
         assert pos.size >= k // 2
         hit = rng.choice(pos, min(k // 2, pos.size), replace=False)
         scores[b, hit] = (50.0 + rng.standard_normal(hit.size)).astype(np.float32)

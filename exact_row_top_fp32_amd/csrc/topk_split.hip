@@ -261,7 +261,7 @@ struct F32Elem {
     __device__ static uint32_t scalar_bits(Scalar x) { return __float_as_uint(x); }
     static constexpr int kKeyShift = 0;  // every key bit carries information
     __device__ static uint32_t full_key(uint32_t v) { return v; }
-    __device__ static SurvivorBound bound(uint32_t T, bool pos) {
+    __device__ __forceinline__ static SurvivorBound bound(uint32_t T, bool pos) {
         const uint32_t t = pos ? (T ^ 0x80000000u) : ~T;
         return SurvivorBound{t, t};
     }
@@ -295,7 +295,7 @@ struct Bf16Elem {
     // as a signed integer, reach t >= 0 exactly when h as a signed 16-bit
     // integer reaches ceil(t / 2^16); as an unsigned integer they stay at or
     // below t exactly when h stays at or below floor(t / 2^16).
-    __device__ static SurvivorBound bound(uint32_t T, bool pos) {
+    __device__ __forceinline__ static SurvivorBound bound(uint32_t T, bool pos) {
         if (pos) {
             const uint32_t t = T ^ 0x80000000u;  // at most 0x7FFFFFFF
             return SurvivorBound{t, (uint32_t)(((uint64_t)t + 0xFFFFu) >> 16)};  // at most 2^15
@@ -320,20 +320,35 @@ struct Bf16Elem {
 template <class E>
 __device__ __forceinline__ uint32_t elem_key(uint32_t bits) { return order_key(__uint_as_float(bits)); }
 
-// Every score of a row in global memory (the full-row selection's source).
+// Every score of a row in global memory (the full-row selection's source),
+// E::kUnroll loads per lane in flight as in the streaming rounds (one at a
+// time, a workgroup reads a long row at a small fraction of its share of the
+// memory bandwidth).
 template <class S, class E>
 struct ElemRowSource {
     const typename E::Scalar* row;
     int64_t len;
     template <class F>
     __device__ void for_each(F&& f) const {
+        constexpr int kU = E::kUnroll;
         const typename E::Vec* rv = reinterpret_cast<const typename E::Vec*>(row);
         const int64_t nvec = len / E::kPerVec;
-        for (int64_t v = S::rank(); v < nvec; v += S::kSize) {
-            const typename E::Vec x = rv[v];
+        for (int64_t v0 = S::rank(); v0 < nvec; v0 += (int64_t)kU * S::kSize) {
+            typename E::Vec x[kU];
 #pragma unroll
-            for (int j = 0; j < E::kPerVec; ++j)
-                f(elem_key<E>(E::bits(x, j)), (uint32_t)(E::kPerVec * v + j));
+            for (int u = 0; u < kU; ++u) {
+                const int64_t v = v0 + (int64_t)u * S::kSize;
+                if (v < nvec) x[u] = rv[v];
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t v = v0 + (int64_t)u * S::kSize;
+                if (v < nvec) {
+#pragma unroll
+                    for (int j = 0; j < E::kPerVec; ++j)
+                        f(elem_key<E>(E::bits(x[u], j)), (uint32_t)(E::kPerVec * v + j));
+                }
+            }
         }
         for (int64_t i = E::kPerVec * nvec + S::rank(); i < len; i += S::kSize)
             f(elem_key<E>(E::scalar_bits(row[i])), (uint32_t)i);
@@ -398,8 +413,8 @@ struct Cutoff {
 };
 
 template <class E, int kRuns = kMaxRuns, class Issue = NoIssue>
-__device__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, SelectLds lds,
-                               Issue&& issue = Issue{}) {
+__device__ __forceinline__ Cutoff short_cutoff(const typename E::Scalar* row, int64_t L, uint32_t m, SelectLds lds,
+                                               Issue&& issue = Issue{}) {
     using B = BlockScope<kThreads>;
     const int64_t fit = L / (2 * kRunLen);
     const int runs = fit < kRuns ? (int)fit : kRuns;

@@ -461,6 +461,24 @@ def test_short_row_threshold_widths(topk, W):
     assert_parity(wl, got, expect(wl))
 
 
+def test_short_rows_past_16384_stay_sampled(topk):
+    # rows of 16385..32768 scores take a sample of 64 runs: at k = 2048 their
+    # survivors (about 1.4 m) stay well inside the 3840-entry buffer, so every
+    # N(0,1) row keeps to the sampled path (with 32 runs, about one such row
+    # in eleven overflowed into the full-row selection)
+    rng = np.random.default_rng(57)
+    B, W, k = 64, 32768, 2048
+    scores = rng.standard_normal((B, W)).astype(np.float32)
+    lengths = rng.integers(16385, W + 1, B).astype(np.int32)
+    lengths[:3] = [16385, W, W - 1]
+    synth.poison_tails(scores, lengths)
+    wl = synth.Workload("short_past_16384", 57, scores, lengths, W, k)
+    got, stats = run(topk, wl, want_stats=True)
+    assert_parity(wl, got, expect(wl))
+    assert np.all(stats[:, 0] == 3), f"rows off the sampled path: {np.unique(stats[:, 0], return_counts=True)}"
+    assert stats[:, 1].max() <= SHORT_CAP and stats[:, 1].min() >= k
+
+
 def test_short_rows_overflow_fallback(topk):
     # rows whose sample hides a crowd just above the cutoff: more survivors
     # than the LDS buffer holds, so the full-row selection runs

@@ -973,9 +973,9 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
     constexpr int64_t kR = (int64_t)kThreads * kU;  // loads per workgroup round
     using B = BlockScope<kThreads>;
     typedef typename E::Vec Vec;
-    // the survivors, as two arrays of words: the word of the load that held
-    // each (words[]) and its position (words[kShortCap + ...]); later the
-    // selection's and the emission's lists
+    // the survivors, seen as words (sw below): sw[e] is the 32-bit load word
+    // that held survivor e, sw[kShortCap + e] its position; later the
+    // selection's member list and the emission's output list
     __shared__ uint2 buf[kShortCap + 64];
     __shared__ uint32_t hist[kBins + 64];
     __shared__ uint32_t found[3];

@@ -1109,7 +1109,9 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
         for (int u = 0; u < kU; ++u) {
 #pragma unroll
             for (int j = 0; j < E::kPerVec; ++j) {
-                if (__builtin_expect(E::template pass<kPos>(x[u], j, sb2), 1)) {  // some lane passes
+                // some lane of the wave nearly always passes: the hint keeps
+                // the compiler from branching around each write
+                if (__builtin_expect(E::template pass<kPos>(x[u], j, sb2), 1)) {
                     *reinterpret_cast<uint32_t*>(bytes + slot) = E::word(x[u], j);
                     *reinterpret_cast<uint32_t*>(bytes + slot + kShortCap * sizeof(uint32_t)) =
                         p0 + (uint32_t)(E::kPerVec * kThreads * u + j);
@@ -1118,10 +1120,10 @@ __global__ __launch_bounds__(kThreads, 4) void short_rows_kernel(SplitParams p) 
             }
         }
     };
-    // The first round is in flight since the sample; a third is loaded into
-    // the first buffer as soon as that has been filtered. Rows past three
-    // rounds (wider than any the short-row path is fast for) go on one round
-    // at a time.
+    // The first round is in flight since the sample, the second since the
+    // cutoff (bf16) or from just after the first is filtered (fp32); a third
+    // is loaded into the first buffer as soon as that has been filtered. Rows
+    // past three rounds go on one round at a time.
     auto stream = [&](auto pos_tag) {
         filter(pos_tag, xa, 0);
         if (kR >= nvec) return;

@@ -91,7 +91,6 @@ __global__ __launch_bounds__(kAmaxThreads) void amax8_kernel(Amax8Params p) {
 constexpr int kTabThreads = 256;
 constexpr int kTabMaxBlocks = 262144;              // blocks per row (2^21 positions)
 constexpr int kTabWords = kTabMaxBlocks / 32;      // bitmap words
-constexpr int kTabWordsPerLane = kTabWords / kTabThreads;
 constexpr int32_t kPad = 0x7FFFFFFF;
 
 struct TableParams {

@@ -58,7 +58,6 @@ constexpr int kRunLen = 64;                     // scores per contiguous sample 
 constexpr int kMaxRuns = 64;                    // sample runs of a split row
 constexpr int kShortRuns = 32;                  // sample runs of a short row up to kShortLong scores
 constexpr int64_t kShortLong = 16384;           // longer short rows take kMaxRuns runs
-constexpr int kMaxSample = kRunLen * kMaxRuns;  // 4096 keys at most
 constexpr int kMaxPieces = 256;                 // workgroups per row at most
 constexpr int kFinThreads = 1024;               // finisher workgroup: 16 waves
 

@@ -1,8 +1,9 @@
 """GPU parity of the split-row mode (topk_select_split) against the CPU oracle.
 
-Each row is cut into pieces, one workgroup each; the last workgroup of a row
-selects from the survivors every piece appended to the row's area of the
-workspace. The result must be the oracle's, index for index, whatever the
+Each row is cut into pieces, one workgroup each; a third launch, one
+workgroup per row, selects from the survivors every piece appended to the
+row's area of the workspace (a full batch with the automatic piece count runs
+one workgroup per row in a single launch instead). The result must be the oracle's, index for index, whatever the
 number of pieces, the row's length (tails of 1-3 scores, pieces with nothing
 to read), the path (sampled, keep-all, full-row, overflow), or what an
 earlier call left in the workspace. Output and workspace sit between guard

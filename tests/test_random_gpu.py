@@ -1,13 +1,14 @@
 """Seeded random cases through every entry point of the short-row and split
 kernels, against the CPU oracle.
 
-Each case draws a width (short and long short-row widths, odd widths with a
-padded row stride), k, a batch of rows of mixed kinds (the adversarial kinds
-of the parity workloads and N(0,1) rows), lengths from -2 to past the width,
-and optionally a page table (page sizes 1, 3, 16, 64 and 100); it runs one of
-`topk_select` (automatic kernel), `topk_select_ex` with the short-row kernel
-and the sampled path forced, or `topk_select_split`, and, for widths of at
-most 16384, `topk_select_bf16` on the same rows rounded to bf16. Every
+Each case draws a width (short-row widths, and in two blocks widths for the
+persistent kernel up to 262144; odd widths with a padded row stride), k, a
+batch of rows of mixed kinds (the adversarial kinds of the parity workloads
+and N(0,1) rows), lengths from -2 to past the width, and optionally a page
+table (page sizes 1, 3, 16, 64 and 100); it runs one of `topk_select`
+(automatic kernel), `topk_select_ex` with the short-row or the persistent
+kernel and the sampled path forced, or `topk_select_split`, and, for widths
+of at most 16384, `topk_select_bf16` on the same rows rounded to bf16. Every
 output is checked against the oracle (values as a multiset of bit patterns,
 positions, -1 padding, page mapping). The pages base the fix's correctness on
 forcing every backend over many cases ("vLLM PR #56346 report", discussion);
@@ -26,9 +27,11 @@ from topk_check import check
 pytestmark = pytest.mark.gpu
 
 WIDTHS = [700, 4096, 9000, 16384, 16385, 20000, 32767, 32768]
+LONG_WIDTHS = [32769, 40000, 65536, 100003, 131072, 262144]
 KS = [1, 7, 64, 511, 512, 1000, 2048]
 KINDS = synth.C2_KINDS + ["normal"] * 8
 ENTRIES = ["auto", "short_sampled", "split"]
+LONG_ENTRIES = ["auto", "persistent_sampled", "split"]
 
 
 @pytest.fixture(scope="module")
@@ -40,8 +43,8 @@ def topk():
     return topk_mod
 
 
-def draw_case(rng):
-    W = int(rng.choice(WIDTHS))
+def draw_case(rng, widths, entries):
+    W = int(rng.choice(widths))
     k = min(int(rng.choice(KS)), max(1, W // 4))  # some row kinds plant k / 2 values
     B = int(rng.integers(1, 40))
     kinds = [str(rng.choice(KINDS)) for _ in range(B)]
@@ -52,15 +55,19 @@ def draw_case(rng):
     synth.poison_tails(wl.scores, wl.lengths)
     ps = int(rng.choice([0, 0, 1, 3, 16, 64, 100]))
     pt = synth._page_table(rng, B, W, ps) if ps else None
-    entry = str(rng.choice(ENTRIES))
+    entry = str(rng.choice(entries))
     return wl, W, k, ps, pt, entry
 
 
-@pytest.mark.parametrize("block", range(4))
-def test_random_cases(topk, block):
+# four blocks of short widths, two of long ones (the persistent kernel)
+BLOCKS = [(b, WIDTHS, ENTRIES, 40) for b in range(4)] + [(4 + b, LONG_WIDTHS, LONG_ENTRIES, 20) for b in range(2)]
+
+
+@pytest.mark.parametrize("block,widths,entries,cases", BLOCKS, ids=[f"block{b[0]}" for b in BLOCKS])
+def test_random_cases(topk, block, widths, entries, cases):
     rng = np.random.default_rng(9100 + block)
-    for case in range(40):
-        wl, W, k, ps, pt_h, entry = draw_case(rng)
+    for case in range(cases):
+        wl, W, k, ps, pt_h, entry = draw_case(rng, widths, entries)
         B = wl.batch
         print(f"  case {block}.{case}: {entry} B={B} W={W} k={k} ps={ps} seed={wl.seed}", flush=True)
         s = torch.from_numpy(wl.scores).cuda()
@@ -71,6 +78,9 @@ def test_random_cases(topk, block):
             topk.topk_select(s, ln, k, out, pt, ps, n_cols=W)
         elif entry == "short_sampled":
             topk.topk_select_ex(s, ln, k, out, pt, ps, n_cols=W, kernel=topk.KERNEL_SHORT, force_path=topk.PATH_SAMPLED)
+        elif entry == "persistent_sampled":
+            topk.topk_select_ex(s, ln, k, out, pt, ps, n_cols=W, kernel=topk.KERNEL_PERSISTENT,
+                                force_path=topk.PATH_SAMPLED)
         else:
             topk.topk_select_split(s, ln, k, out, pt, ps, n_cols=W)
         torch.cuda.synchronize()

@@ -108,6 +108,9 @@ __device__ __forceinline__ uint32_t wave_reserve_count(uint32_t* counter, uint32
 }
 
 __device__ __forceinline__ f4 load_nt(const f4* p) { return __builtin_nontemporal_load(p); }
+// A selection's output, written once and never read back by the kernel:
+// streamed past the L2 so that it takes no lines the rows' loads still use.
+__device__ __forceinline__ void store_nt(int32_t* p, int32_t v) { __builtin_nontemporal_store(v, p); }
 
 // ----------------------------------------------------------------------------
 // cooperative scopes

@@ -889,7 +889,7 @@ __device__ __forceinline__ void emit_slots(const RegPairs<N>& sv, Selection sel,
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const uint32_t j = (uint32_t)(i * B::kSize) + threadIdx.x;
-        if (j < m) row[j] = (int32_t)o[i];
+        if (j < m) store_nt(row + j, (int32_t)o[i]);
     }
 }
 
